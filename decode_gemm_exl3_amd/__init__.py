@@ -1,0 +1,140 @@
+"""Python binding of the EXL3 decode-matmul library (libexl3.so, HIP for gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/exl3.h.  PyTorch supplies device
+memory and the current stream.  If the library has not been built, every call
+raises; there is no other implementation behind these names.
+
+Tensors:
+  words / trellis : int16 (uint16 bit patterns), trellis shape [n_out/16, n_in/16, 16*bits]
+  x               : float16 [m, n_in]
+  sign            : float16 [n_in] (+-1)
+  out_scale       : float16 [n_out]
+  result y        : float16 [m, n_out]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemm",
+           "status_string"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class Exl3Error(RuntimeError):
+    pass
+
+
+def lib_path() -> str:
+    return os.environ.get("EXL3_LIB", os.path.join(_PKG, "libexl3.so"))
+
+
+class _PackInfo(ctypes.Structure):
+    _fields_ = [("n_in", ctypes.c_int32), ("n_out", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("max_m", ctypes.c_int32), ("tiles_in", ctypes.c_int32), ("tiles_out", ctypes.c_int32),
+                ("words_per_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("trellis_words", ctypes.c_int64), ("trellis_bytes", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_int64)]
+
+
+def load() -> ctypes.CDLL:
+    """Load libexl3.so once; raise if it is missing (no fallback path exists)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = lib_path()
+    if not os.path.exists(path):
+        raise Exl3Error(f"{path} not found: build it with decode_gemm_exl3_amd._build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.exl3_pack_info.argtypes = [i32, i32, i32, i32, ctypes.POINTER(_PackInfo)]
+    lib.exl3_pack_info.restype = ctypes.c_int
+    lib.exl3_decode_tile.argtypes = [vp, i32, i64, vp, vp]
+    lib.exl3_decode_tile.restype = ctypes.c_int
+    for name in ("exl3_gemv", "exl3_gemm"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
+        f.restype = ctypes.c_int
+    lib.exl3_status_string.argtypes = [ctypes.c_int]
+    lib.exl3_status_string.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().exl3_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise Exl3Error(f"{what}: {status_string(status)} ({status})")
+
+
+def pack_info(n_in: int, n_out: int, bits: int, max_m: int = 1) -> dict:
+    info = _PackInfo()
+    _check(load().exl3_pack_info(n_in, n_out, bits, max_m, ctypes.byref(info)), "exl3_pack_info")
+    return {f: getattr(info, f) for f, _ in _PackInfo._fields_ if f != "reserved"}
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Workspace:
+    """Device scratch sized by exl3_pack_info for (n_in, n_out, bits, max_m).
+
+    Needs no initialisation; one workspace per stream of concurrent calls.
+    """
+
+    def __init__(self, n_in: int, n_out: int, bits: int, max_m: int, device="cuda"):
+        import torch
+        self.info = pack_info(n_in, n_out, bits, max_m)
+        self.nbytes = int(self.info["workspace_bytes"])
+        self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+
+    def fits(self, n_in: int, n_out: int, bits: int, m: int) -> bool:
+        return pack_info(n_in, n_out, bits, max(m, 1))["workspace_bytes"] <= self.nbytes
+
+
+def decode_tile(words, bits: int, out=None, stream=None):
+    """Decode packed tiles [T, 16*bits] (int16) to fp16 [T, 256] in trellis order."""
+    import torch
+    T = words.shape[0]
+    if out is None:
+        out = torch.empty((T, 256), dtype=torch.float16, device=words.device)
+    _check(load().exl3_decode_tile(_ptr(words), bits, T, _ptr(out), _stream(stream)), "exl3_decode_tile")
+    return out
+
+
+def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
+    import torch
+    m, n_in = x.shape
+    n_out = out_scale.shape[0]
+    if y is None:
+        y = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
+    if workspace is None:
+        workspace = Workspace(n_in, n_out, bits, max(m, 1), device=x.device)
+    rc = getattr(load(), fn)(_ptr(x), m, _ptr(trellis), _ptr(sign), _ptr(out_scale), n_in, n_out, bits,
+                             _ptr(y), _ptr(workspace.buf), workspace.nbytes, _stream(stream))
+    _check(rc, fn)
+    return y
+
+
+def gemv(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
+    """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 8 (fp16 out)."""
+    return _linear("exl3_gemv", x, trellis, sign, out_scale, bits, workspace, y, stream)
+
+
+def gemm(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
+    """The same result for any m >= 1 through the matrix-core GEMM path."""
+    return _linear("exl3_gemm", x, trellis, sign, out_scale, bits, workspace, y, stream)

@@ -1,0 +1,199 @@
+// exl3_api.hip - the C ABI: argument checks, workspace layout, dispatch.
+#include <atomic>
+#include <cstdlib>
+
+#include "../../include/exl3.h"
+#include "exl3_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Optional override of the number of input chunks of a GEMV (tuning sweeps).
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+int cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Workspace needs.  Nothing in the workspace survives between calls, so each
+// call lays out only what it uses from offset 0:
+//   gemv: nothing (one kernel, partial sums stay in LDS);
+//   gemm: the rotated input, fp16 [m][n_in].
+int64_t gemv_ws_bytes(int n_out, int m) { (void)n_out; (void)m; return 0; }
+int64_t gemm_ws_bytes(int n_in, int m) { return align256((int64_t)m * n_in * 2); }
+int64_t ws_total(int n_in, int n_out, int max_m) {
+    const int64_t a = gemv_ws_bytes(n_out, max_m < 8 ? max_m : 8);
+    const int64_t b = gemm_ws_bytes(n_in, max_m);
+    return a > b ? a : b;
+}
+
+// GEMV launch plan.  Persistent workgroups (about one per CU) own strips
+// round-robin.  The input dimension is cut into as few chunks as the LDS budget
+// allows (x' of a chunk lives in LDS).  Within a strip, W waves share the steps
+// (4 tile columns each); W, the steps per wave (nsw) and the steps in flight
+// (pf, nsw % pf == 0) are picked to waste few padded steps while keeping many
+// loads in flight.
+bool plan_gemv(exl3::GemvParams* p) {
+    static const int nk_force = env_int("EXL3_GEMV_KCHUNKS", 0);
+    static const int grid_mul = env_int("EXL3_GEMV_GRID_PER_CU", 1);
+    int grid = cu_count() * grid_mul;
+    if (grid > p->n_strips) grid = p->n_strips;
+    const int nj = (p->n_strips + grid - 1) / grid;
+    for (int nk = nk_force > 0 ? nk_force : 1; nk <= p->tiles_in / 8; ++nk) {
+        int kc = (p->tiles_in + nk - 1) / nk;
+        kc = (kc + 7) & ~7;
+        const int n_kchunks = (p->tiles_in + kc - 1) / kc;
+        const int steps = (kc + 3) / 4;
+        double best = 1e30;
+        int bw = 0, bn = 0, bp = 0;
+        static const int pf_force = env_int("EXL3_GEMV_PF", 0);
+        static const int w_force = env_int("EXL3_GEMV_WAVES", 0);
+        for (int pf : {8, 4, 2}) {
+            if (pf_force > 0 && pf != pf_force) continue;
+            for (int w = 16; w >= 4; --w) {
+                if (w_force > 0 && w != w_force) continue;
+                int nsw = (steps + w - 1) / w;
+                nsw = (nsw + pf - 1) / pf * pf;
+                const double penalty = pf == 8 ? 1.0 : (pf == 4 ? 1.06 : 1.2);
+                const double cost = (double)w * nsw * penalty + 0.01 * (16 - w);
+                if (exl3::gemv_lds_bytes(p->m, w, nsw, pf, nj) > (size_t)exl3::GEMV_LDS_BUDGET) continue;
+                if (cost < best) { best = cost; bw = w; bn = nsw; bp = pf; }
+            }
+        }
+        if (bw == 0) {
+            if (nk_force > 0) return false;
+            continue;
+        }
+        p->kc = kc;
+        p->n_kchunks = n_kchunks;
+        p->waves = bw;
+        p->nsw = bn;
+        p->pf = bp;
+        p->grid = grid;
+        return true;
+    }
+    return false;
+}
+
+bool bad_shape(int32_t n_in, int32_t n_out, int32_t bits) {
+    return n_in <= 0 || n_out <= 0 || (n_in % 128) != 0 || (n_out % 16) != 0 || bits < 1 || bits > 8;
+}
+
+int common_checks(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+                  const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
+                  void* workspace, size_t workspace_bytes, int64_t need) {
+    if (m < 0 || bad_shape(n_in, n_out, bits)) return EXL3_EINVAL;
+    if (m == 0) return EXL3_OK;
+    if (!x || !trellis || !sign || !out_scale || !y) return EXL3_EINVAL;
+    if ((const void*)x == (const void*)y) return EXL3_EINVAL;
+    if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return EXL3_EWORKSPACE;
+    // weights are read through 32-bit buffer offsets
+    if ((int64_t)n_in * n_out * bits / 8 >= ((int64_t)1 << 31) - ((int64_t)1 << 20)) return EXL3_EUNSUPPORTED;
+    return 1;  // proceed
+}
+
+}  // namespace
+
+extern "C" {
+
+int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m, exl3_pack_info_t* out) {
+    if (!out || max_m < 1 || bad_shape(n_in, n_out, bits)) return EXL3_EINVAL;
+    out->n_in = n_in;
+    out->n_out = n_out;
+    out->bits = bits;
+    out->max_m = max_m;
+    out->tiles_in = n_in / 16;
+    out->tiles_out = n_out / 16;
+    out->words_per_tile = 16 * bits;
+    out->reserved = 0;
+    out->trellis_words = (int64_t)out->tiles_in * out->tiles_out * out->words_per_tile;
+    out->trellis_bytes = (int64_t)n_in * n_out * bits / 8;
+    out->workspace_bytes = ws_total(n_in, n_out, max_m);
+    return EXL3_OK;
+}
+
+int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles, uint16_t* out, void* stream) {
+    if (bits < 1 || bits > 8 || n_tiles < 0) return EXL3_EINVAL;
+    if (n_tiles == 0) return EXL3_OK;
+    if (!words || !out) return EXL3_EINVAL;
+    if (n_tiles > (int64_t)0xFFFFFFFF * 16) return EXL3_EUNSUPPORTED;
+    hipError_t e = exl3::launch_decode(bits, words, n_tiles, out, (hipStream_t)stream);
+    return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+}
+
+int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+              const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
+              void* workspace, size_t workspace_bytes, void* stream) {
+    if (m > 8) return EXL3_EINVAL;
+    const int mm = m > 0 ? m : 1;
+    int rc = common_checks(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes,
+                           gemv_ws_bytes(n_out, mm));
+    if (rc <= 0) return rc;
+    exl3::GemvParams p;
+    p.x = x;
+    p.trellis = trellis;
+    p.sign = sign;
+    p.out_scale = out_scale;
+    p.y = y;
+    p.m = m;
+    p.n_in = n_in;
+    p.n_out = n_out;
+    p.tiles_in = n_in / 16;
+    p.n_strips = n_out / 16;
+    if (!plan_gemv(&p)) return EXL3_EUNSUPPORTED;
+    hipError_t e = exl3::launch_gemv(bits, p, (hipStream_t)stream);
+    return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+}
+
+int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+              const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
+              void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = common_checks(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes,
+                           gemm_ws_bytes(n_in, m > 0 ? m : 1));
+    if (rc <= 0) return rc;
+    if ((int64_t)m > (int64_t)65535 * 64) return EXL3_EUNSUPPORTED;
+    uint16_t* xr = static_cast<uint16_t*>(workspace);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = exl3::launch_rotate(x, sign, m, n_in, xr, s);
+    if (e != hipSuccess) return EXL3_EHIP;
+    exl3::GemmParams p;
+    p.xr = xr;
+    p.trellis = trellis;
+    p.out_scale = out_scale;
+    p.y = y;
+    p.m = m;
+    p.n_in = n_in;
+    p.n_out = n_out;
+    p.tiles_in = n_in / 16;
+    p.n_strips = n_out / 16;
+    e = exl3::launch_gemm(bits, p, s);
+    return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+}
+
+const char* exl3_status_string(int status) {
+    switch (status) {
+        case EXL3_OK: return "ok";
+        case EXL3_EINVAL: return "invalid argument";
+        case EXL3_EUNSUPPORTED: return "unsupported request";
+        case EXL3_EWORKSPACE: return "workspace missing or too small";
+        case EXL3_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,169 @@
+// exl3_device.hpp - device building blocks shared by the EXL3 kernels (gfx950).
+//
+// Trellis rows.  A 16x16 tile is a cyclic stream of 256*K bits (16K uint16
+// words, LSB first).  Row n of the tile holds states 16n..16n+15, whose 16-bit
+// windows start at stream bits 16nK + cK (c = 0..15) and reach at most 15 bits
+// into the next row; row 15 wraps to the start of the tile (tail-biting).  One
+// lane owns one row: it loads ceil(K/2) dwords starting at dword floor(nK/2),
+// and the one dword it still needs comes from the lane that owns row n+1 (row
+// 0 for row 15) through a DPP row rotation inside its 16-lane row, so the
+// tile's wrap costs nothing.
+//
+// Codebook (table-free; pages: "GEMM kernel" - one integer multiply plus one
+// three-input bit operation per index; "conclusion first" - three instructions):
+//   p = s*A + B (mod 2^32)      v_mad_u32_u16, state read from either 16-bit half
+//   q = (p & M) | X             v_and_or_b32
+//   value = lo(q) + hi(q)       fp16 add, or left to the matrix core (two k slots)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+constexpr uint32_t CB_A = 0xBFD3u;
+constexpr uint32_t CB_B = 0x201784FFu;
+constexpr uint32_t CB_M = 0x8D7F8DFFu;
+constexpr uint32_t CB_X = 0x30003000u;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <int K> struct RowGeom {
+    static constexpr int KD = (K + 1) / 2;   // dwords a lane loads for its row
+    static constexpr int NB = KD + 1;        // plus the neighbour's first dword
+    static constexpr int DW_PER_TILE = 8 * K;
+};
+
+// Register-held codebook constants.  A VOP3 instruction on gfx9 reads at most
+// one SGPR or literal, so B and X live in VGPRs and A and M in SGPRs.  They are
+// produced by opaque moves so the compiler cannot fold them back into literals
+// (which would split the mask-and-plant into two instructions).
+struct CbRegs {
+    uint32_t vB, vX, sM;
+};
+
+__device__ __forceinline__ CbRegs cb_regs() {
+    CbRegs r;
+    uint32_t b = CB_B, x = CB_X, m = CB_M;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r.vB) : "s"(b));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r.vX) : "s"(x));
+    asm volatile("s_mov_b32 %0, %1" : "=s"(r.sM) : "s"(m));
+    return r;
+}
+
+// The multiply reads the state from either 16-bit half of a register
+// (v_mad_u32_u16 with op_sel), which has no C spelling, so it is inline asm.
+// The mask-and-plant stays in C: it feeds the matrix core, and the compiler must
+// see that VALU write to insert the wait states an MFMA source read requires.
+__device__ __forceinline__ uint32_t cb_mask(uint32_t p, const CbRegs& r) { return (p & r.sM) | r.vX; }
+
+// Codebook word for the state held in the low 16 bits of w.
+__device__ __forceinline__ uint32_t cb_lo(uint32_t w, const CbRegs& r) {
+    uint32_t p;
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(p) : "v"(w), "s"(CB_A), "v"(r.vB));
+    return cb_mask(p, r);
+}
+
+// Codebook word for the state held in the high 16 bits of w.
+__device__ __forceinline__ uint32_t cb_hi(uint32_t w, const CbRegs& r) {
+    uint32_t p;
+    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(p) : "v"(w), "s"(CB_A), "v"(r.vB));
+    return cb_mask(p, r);
+}
+
+// fp16 sum of the two halves of a codebook word, round to nearest even.
+__device__ __forceinline__ uint16_t cb_sum(uint32_t q) {
+    __half lo = __ushort_as_half((unsigned short)(q & 0xFFFFu));
+    __half hi = __ushort_as_half((unsigned short)(q >> 16));
+    return __half_as_ushort(__hadd(lo, hi));
+}
+
+// Dword of the lane that owns the next row of the same tile (row 15 -> row 0):
+// DPP row_ror:15 inside each 16-lane row.
+__device__ __forceinline__ uint32_t next_row_dword(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x12F, 0xF, 0xF, false);
+}
+
+// Byte offset of row n's first loaded dword (dword floor(nK/2)) inside its tile.
+template <int K>
+__device__ __forceinline__ uint32_t row_offset(int n) {
+    return (uint32_t)(((n * K) >> 1) * 4);
+}
+
+// Buffer resource over [base, base + bytes): loads at or past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int nrec = bytes <= 0 ? 0 : (bytes >= 0x7FFFFFF0 ? 0x7FFFFFF0 : (int)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nrec, 0x00020000);
+}
+
+constexpr int kNT = 2;  // streaming (non-temporal) cache policy for the weight stream
+
+// Load the lane's row: ceil(K/2) dwords at byte voff + soff of the buffer.
+// voff is the per-lane offset (row_offset included), soff a wave-uniform step
+// offset, so the address costs no vector instruction.
+template <int K>
+__device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t soff,
+                                         uint32_t (&b)[RowGeom<K>::NB]) {
+    constexpr int KD = RowGeom<K>::KD;
+    if constexpr (KD == 1) {
+        b[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kNT);
+    } else if constexpr (KD == 2) {
+        u32x2_t v = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kNT));
+        b[0] = v.x; b[1] = v.y;
+    } else if constexpr (KD == 3) {
+        typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+        u32x3_t v = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(rs, voff, soff, kNT));
+        b[0] = v.x; b[1] = v.y; b[2] = v.z;
+    } else {
+        u32x4_t v = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kNT));
+        b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+    }
+}
+
+// Complete a loaded row: fetch the neighbour dword and, for odd K on odd rows
+// (which start 16 bits into their first dword), shift the row so that state c
+// always starts at bit cK of b[].
+template <int K>
+__device__ __forceinline__ void finish_row(int n, uint32_t (&b)[RowGeom<K>::NB]) {
+    constexpr int KD = RowGeom<K>::KD;
+    b[KD] = next_row_dword(b[0]);
+    if constexpr (K & 1) {
+        const uint32_t sh = (uint32_t)((n & 1) << 4);
+#pragma unroll
+        for (int k = 0; k < KD; ++k) b[k] = __builtin_amdgcn_alignbit(b[k + 1], b[k], sh);
+    }
+}
+
+// Codebook words of the 16 states of a finished row: q[c] for state c.
+// All offsets are compile-time constants; windows at bit 0 or 16 of a dword are
+// read in place, and when K divides 16 one funnel shift serves two states.
+template <int K>
+__device__ __forceinline__ void decode_row(const uint32_t (&b)[RowGeom<K>::NB], uint32_t (&q)[16],
+                                           const CbRegs& r) {
+    constexpr int NB = RowGeom<K>::NB;
+    constexpr bool pairs = (16 % K) == 0;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        const int P = c * K;
+        const int dw = P >> 5;
+        const int sh = P & 31;
+        if (sh == 0) {
+            q[c] = cb_lo(b[dw], r);
+        } else if (sh == 16) {
+            q[c] = cb_hi(b[dw], r);
+        } else if (pairs && sh > 16) {
+            // produced together with state c - 16/K (same funnel shift, high half)
+        } else {
+            // a window that ends inside b[dw] may take any high operand
+            const uint32_t w = __builtin_amdgcn_alignbit(b[(dw + 1 < NB) ? dw + 1 : dw], b[dw],
+                                                         (uint32_t)sh);
+            q[c] = cb_lo(w, r);
+            if (pairs && c + 16 / K < 16) q[(c + 16 / K) & 15] = cb_hi(w, r);
+        }
+    }
+}
+
+}  // namespace exl3

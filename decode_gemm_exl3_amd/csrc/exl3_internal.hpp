@@ -1,0 +1,46 @@
+// exl3_internal.hpp - host/device interface between the C ABI and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace exl3 {
+
+constexpr int GEMV_LDS_BUDGET = 160 * 1024;  // bytes of LDS per GEMV workgroup (one per CU)
+
+struct GemvParams {
+    const uint16_t* x;
+    const uint16_t* trellis;
+    const uint16_t* sign;
+    const uint16_t* out_scale;
+    uint16_t* y;
+    int m, n_in, n_out;
+    int tiles_in, n_strips;
+    int kc;             // tile columns per input chunk (x' of a chunk sits in LDS)
+    int n_kchunks;      // input chunks
+    int waves;          // waves per workgroup
+    int nsw;            // steps (4 tile columns each) per wave per strip, a multiple of pf
+    int pf;             // steps in flight per wave
+    int grid;           // persistent workgroups; workgroup b owns strips b, b + grid, ...
+};
+
+// LDS of a GEMV workgroup: x' rows, a zero block, per-wave partial sums of its nj strips.
+__host__ __device__ inline size_t gemv_lds_bytes(int m, int waves, int nsw, int pf, int nj) {
+    return ((size_t)m * waves * nsw * 64 + (size_t)pf * 64 + (size_t)nj * waves * m * 16) * 4;
+}
+
+struct GemmParams {
+    const uint16_t* xr;     // rotated input, fp16 [m][n_in] (x'/128)
+    const uint16_t* trellis;
+    const uint16_t* out_scale;
+    uint16_t* y;
+    int m, n_in, n_out;
+    int tiles_in, n_strips;
+};
+
+hipError_t launch_decode(int K, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s);
+hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr,
+                         hipStream_t s);
+hipError_t launch_gemv(int K, const GemvParams& p, hipStream_t s);
+hipError_t launch_gemm(int K, const GemmParams& p, hipStream_t s);
+
+}  // namespace exl3

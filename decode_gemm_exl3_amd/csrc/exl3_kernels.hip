@@ -1,0 +1,363 @@
+// exl3_kernels.hip - decode, input rotation and GEMV kernels for gfx950.
+#include "exl3_device.hpp"
+#include "exl3_internal.hpp"
+
+namespace exl3 {
+
+// ---------------------------------------------------------------------------
+// decode_tile: one wave decodes 4 tiles, lane (n, g) = row n of tile 4*wave + g.
+// Output is the fp16 sum of the halves (bit-exact codebook value), in trellis
+// order: element 16n + c of the tile.
+// ---------------------------------------------------------------------------
+template <int K>
+__global__ __launch_bounds__(256) void decode_tile_kernel(const uint16_t* __restrict__ words,
+                                                          int64_t n_tiles, uint16_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    const int n = lane & 15;
+    constexpr int64_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
+    const int64_t tile0 = (int64_t)blockIdx.x * 16;
+    const int64_t tile = tile0 + (threadIdx.x >> 6) * 4 + (lane >> 4);
+    const bool valid = tile < n_tiles;
+    const CbRegs cr = cb_regs();
+    // tiles past the end read as zero through the buffer range check
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(reinterpret_cast<const char*>(words) + tile0 * TILE_B, (n_tiles - tile0) * TILE_B);
+    uint32_t b[RowGeom<K>::NB];
+    load_row<K>(rs, (uint32_t)((tile - tile0) * TILE_B) + row_offset<K>(n), 0u, b);
+    finish_row<K>(n, b);  // every lane takes part in the DPP
+    uint32_t q[16];
+    decode_row<K>(b, q, cr);
+    if (valid) {
+        uint32_t o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (uint32_t)cb_sum(q[2 * j]) | ((uint32_t)cb_sum(q[2 * j + 1]) << 16);
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + tile * 256 + n * 16);
+        dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+        dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 128-point Hadamard of one block held by one wave: lane l has elements l and
+// l + 64.  Butterfly stages in natural (Sylvester) order.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fwht128_wave(float& v0, float& v1, int lane) {
+    float a = v0 + v1, d = v0 - v1;
+    v0 = a;
+    v1 = d;
+#pragma unroll
+    for (int h = 32; h >= 1; h >>= 1) {
+        const float u0 = __shfl_xor(v0, h, 64);
+        const float u1 = __shfl_xor(v1, h, 64);
+        const bool up = (lane & h) != 0;
+        v0 = up ? (u0 - v0) : (v0 + u0);
+        v1 = up ? (u1 - v1) : (v1 + u1);
+    }
+}
+
+// 128-point Hadamard of one block held by 16 lanes (one DPP row), 8 values per
+// lane: lane l16 holds elements 8*l16 + e, e = 0..7.  Stages on index bits 0..2
+// are in-lane; bits 3..6 are lane bits 0..3, exchanged with DPP: xor 1 and xor 2
+// by quad permutes, xor 4 as half-row mirror then quad xor 3, xor 8 as row
+// mirror then half-row mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float lane_xor(float v, int h) {
+    switch (h) {
+        case 1: return dpp_f<0xB1>(v);                     // quad_perm [1,0,3,2]
+        case 2: return dpp_f<0x4E>(v);                     // quad_perm [2,3,0,1]
+        case 4: return dpp_f<0x1B>(dpp_f<0x141>(v));       // half-row mirror, quad [3,2,1,0]
+        default: return dpp_f<0x141>(dpp_f<0x140>(v));     // row mirror, half-row mirror
+    }
+}
+
+__device__ __forceinline__ void fwht128_row(float (&v)[8], int l16) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & h) == 0) {
+                const float a = v[e], b = v[e + h];
+                v[e] = a + b;
+                v[e + h] = a - b;
+            }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1) {
+        const bool up = (l16 & h) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float u = lane_xor(v[e], h);
+            v[e] = up ? (u - v[e]) : (v[e] + u);
+        }
+    }
+}
+
+// x'/128 rounded to fp16: exact power-of-two scaling keeps any fp16 input in range.
+__device__ __forceinline__ uint16_t rot_to_half(float v) {
+    return __half_as_ushort(__float2half_rn(v * (1.0f / 128.0f)));
+}
+
+// ---------------------------------------------------------------------------
+// rotate: xr[r][k] = fp16((H128 (sign * x[r]))[k] / 128), one wave per block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ sign, int m, int n_in,
+                                                     uint16_t* __restrict__ xr) {
+    const int lane = threadIdx.x & 63;
+    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nblk_row = n_in >> 7;
+    if (blk >= (int64_t)m * nblk_row) return;
+    const int64_t row = blk / nblk_row;
+    const int col0 = (int)(blk % nblk_row) << 7;
+    const uint16_t* xp = x + row * n_in + col0;
+    float v0 = __half2float(__ushort_as_half(xp[lane])) * __half2float(__ushort_as_half(sign[col0 + lane]));
+    float v1 = __half2float(__ushort_as_half(xp[lane + 64])) *
+               __half2float(__ushort_as_half(sign[col0 + lane + 64]));
+    fwht128_wave(v0, v1, lane);
+    uint16_t* o = xr + row * n_in + col0;
+    o[lane] = rot_to_half(v0);
+    o[lane + 64] = rot_to_half(v1);
+}
+
+// ---------------------------------------------------------------------------
+// GEMV (small m).
+//
+// Matrix-core mapping (v_mfma_f32_16x16x32_f16, D[16x16] += A[16x32] B[32x16]):
+//   B = weights.  Lane (n, g) supplies column n and the k slots of lane group g:
+//       row n of tile 4*step + g of a strip, 4 weights per MFMA, each weight as
+//       its two fp16 codebook halves in two k slots, so the matrix core also adds
+//       the halves.  Each lane decodes its whole row (16 weights) per step.
+//   A = rotated input.  Row r < m of A holds x'[r] (duplicated to match the two
+//       halves) for the inputs of each lane group; rows r >= m are zero.
+//   D[r][n] accumulates y[r][16*strip + n]; lane (n, g) holds D[4g + i][n].
+// A step is one wave-wide load of 4 consecutive tiles of a strip (4 * 32K
+// contiguous bytes).
+//
+// Persistent workgroups: workgroup b owns strips b, b + G, b + 2G, ... (G =
+// grid size, about one workgroup per CU).  The input dimension is cut into
+// chunks whose rotated input fits in LDS (usually one chunk).  For each chunk
+// the workgroup rotates x into LDS once and then walks its strips; within a
+// strip the W waves take consecutive runs of nsw steps.  Every wave keeps PF
+// steps in flight and its load stream runs on across strip and chunk
+// boundaries, so memory latency is paid once per launch rather than once per
+// strip.  Per-wave partial sums live in LDS (each wave owns its slots, no
+// barrier); at the end the waves' sums are added and y is written.  One kernel,
+// no cross-workgroup reduction.
+// ---------------------------------------------------------------------------
+template <int K, int PF>
+__global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
+    // LDS: x' rows [m][xcols] | zero block [PF * 64] | partial sums [nj][W][m][16]
+    extern __shared__ __align__(16) uint32_t xs[];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15;
+    const int g = lane >> 4;
+    const int M = p.m;
+    const int W = p.waves;
+    const int nsw = p.nsw;                 // steps per wave per (strip, chunk), a multiple of PF
+    const int xcols = W * nsw * 64;        // dwords per LDS row
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int nj = (p.n_strips - b + G - 1) / G;   // strips of this workgroup
+    const int nseg = nj * p.n_kchunks;             // (chunk, strip) segments, chunk-major
+
+    uint32_t* zero = xs + M * xcols;
+    float* red = reinterpret_cast<float*>(zero + PF * 64);
+
+    // Weight rows come through one buffer resource over the whole matrix: the
+    // per-step offset is a scalar, the lane offset fixed; reads past the end
+    // (prefetch after the last segment) return zero.
+    constexpr uint32_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
+    constexpr uint32_t STEP_B = 4 * TILE_B;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(p.trellis, (int64_t)p.n_strips * p.tiles_in * TILE_B);
+    const uint32_t loff = (uint32_t)g * TILE_B + row_offset<K>(n);
+    const int col0 = 4 * wave * nsw;  // first tile column of this wave inside a chunk
+    // byte offset of step 0 of segment q (chunk q / nj, strip b + (q % nj) * G)
+    auto seg_off = [&](int q) -> uint32_t {
+        if (q >= nseg) return 0x7FFFFFF0u;  // past the end: zeros
+        const int c = q / nj, j = q % nj;
+        return (uint32_t)(((int64_t)(b + j * G) * p.tiles_in + c * p.kc + col0) * TILE_B);
+    };
+
+    // ---- weight stream first --------------------------------------------------
+    uint32_t buf[PF][RowGeom<K>::NB];
+    {
+        const uint32_t o0 = seg_off(0);
+#pragma unroll
+        for (int u = 0; u < PF; ++u) load_row<K>(rs, loff, o0 + u * STEP_B, buf[u]);
+    }
+    for (int i = tid; i < PF * 64; i += 64 * W) zero[i] = 0u;
+    for (int i = tid; i < nj * W * M * 16; i += 64 * W) red[i] = 0.f;
+
+    const bool adata = n < M;
+    const CbRegs cr = cb_regs();
+    int q = 0;
+    for (int c = 0; c < p.n_kchunks; ++c) {
+        const int tc0 = c * p.kc;
+        const int kcount = min(p.kc, p.tiles_in - tc0);
+        // ---- rotate chunk c of x into LDS: xs[r][k] = dup(fp16(x'/128)) -------
+        if (c > 0) __syncthreads();  // every wave is done with the previous chunk
+        for (int i = kcount * 16 + tid; i < xcols; i += 64 * W)
+            for (int r = 0; r < M; ++r) xs[r * xcols + i] = 0u;
+        {
+            // 16 lanes per 128-input block, 8 inputs per lane (one 16-byte load)
+            const int nblk = (kcount * 16) >> 7;
+            const int l16 = lane & 15;
+            for (int blk = tid >> 4; blk < M * nblk; blk += 4 * W) {
+                const int r = blk / nblk, bb = blk % nblk;
+                const int col = tc0 * 16 + bb * 128 + l16 * 8;
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)r * p.n_in + col);
+                const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(p.sign + col);
+                float v[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t xw = xv[e >> 1], sw = sv[e >> 1];
+                    const int sh = (e & 1) * 16;
+                    v[e] = __half2float(__ushort_as_half((unsigned short)(xw >> sh))) *
+                           __half2float(__ushort_as_half((unsigned short)(sw >> sh)));
+                }
+                fwht128_row(v, l16);
+                uint32_t d[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t h = rot_to_half(v[e]);
+                    d[e] = h | (h << 16);
+                }
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + bb * 128 + l16 * 8);
+                dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
+                dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+            }
+        }
+        __syncthreads();
+
+        for (int j = 0; j < nj; ++j, ++q) {
+            // this segment's x' fragments: data lanes walk their row, others read zeros
+            const uint32_t* ap = adata ? xs + n * xcols + wave * nsw * 64 + g * 16 : zero;
+            const int astep = adata ? PF * 64 : 0;
+            const uint32_t cur = seg_off(q), nxt = seg_off(q + 1);
+            // one accumulator per MFMA of a step: no back-to-back dependent MFMAs
+            f32x4_t acc[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < nsw; st += PF) {
+                // refills of this round target the next round: same segment or the next
+                const uint32_t roff = (st + PF < nsw) ? cur + (st + PF) * STEP_B : nxt;
+#pragma unroll
+                for (int u = 0; u < PF; ++u) {
+                    // x' fragments first: their LDS latency hides behind the decode
+                    u32x4_t av[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const u32x4_t*>(ap + u * 64 + 4 * t);
+                    // decode in place, then refill the same registers: no copies,
+                    // so the wait before each step covers only its own load
+                    finish_row<K>(n, buf[u]);
+                    uint32_t qq[16];
+                    decode_row<K>(buf[u], qq, cr);
+                    __builtin_amdgcn_sched_barrier(0);
+                    load_row<K>(rs, loff, roff + u * STEP_B, buf[u]);
+                    // the refill stays here: the scheduler would otherwise sink the
+                    // loads of the round to its end and expose the memory latency
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const u32x4_t bv = u32x4_t{qq[4 * t], qq[4 * t + 1], qq[4 * t + 2], qq[4 * t + 3]};
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[t]),
+                                                                         __builtin_bit_cast(half8_t, bv), acc[t], 0, 0, 0);
+                    }
+                }
+                ap += astep;
+            }
+            // this wave's partial for strip j (its own slots: no barrier needed)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * g + i;
+                if (r < M) red[((j * W + wave) * M + r) * 16 + n] += (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+            }
+        }
+    }
+
+    // ---- add the W waves' partial sums and write y ------------------------------
+    __syncthreads();
+    for (int idx = tid; idx < nj * M * 16; idx += 64 * W) {
+        const int j = idx / (M * 16), r = (idx >> 4) % M, cc = idx & 15;
+        float v = 0.f;
+        for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + r) * 16 + cc];
+        const int o = (b + j * G) * 16 + cc;
+        const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
+        p.y[(int64_t)r * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * v));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launchers
+// ---------------------------------------------------------------------------
+template <int K>
+static hipError_t launch_decode_k(const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s) {
+    const int64_t blocks = (n_tiles + 15) / 16;
+    hipLaunchKernelGGL(decode_tile_kernel<K>, dim3((unsigned)blocks), dim3(256), 0, s, words, n_tiles, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(int K, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s) {
+    switch (K) {
+        case 1: return launch_decode_k<1>(words, n_tiles, out, s);
+        case 2: return launch_decode_k<2>(words, n_tiles, out, s);
+        case 3: return launch_decode_k<3>(words, n_tiles, out, s);
+        case 4: return launch_decode_k<4>(words, n_tiles, out, s);
+        case 5: return launch_decode_k<5>(words, n_tiles, out, s);
+        case 6: return launch_decode_k<6>(words, n_tiles, out, s);
+        case 7: return launch_decode_k<7>(words, n_tiles, out, s);
+        case 8: return launch_decode_k<8>(words, n_tiles, out, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr, hipStream_t s) {
+    const int64_t blocks = ((int64_t)m * (n_in >> 7) + 3) / 4;
+    hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, sign, m, n_in, xr);
+    return hipGetLastError();
+}
+
+template <int K, int PF>
+static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
+    const size_t lds = gemv_lds_bytes(p.m, p.waves, p.nsw, PF, (p.n_strips + p.grid - 1) / p.grid);
+    static bool attr_set = false;  // allow more than 64 KB of dynamic LDS
+    if (!attr_set) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_BUDGET);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((gemv_kernel<K, PF>), dim3(p.grid), dim3(64 * p.waves), lds, s, p);
+    return hipGetLastError();
+}
+
+template <int K>
+static hipError_t launch_gemv_k(const GemvParams& p, hipStream_t s) {
+    switch (p.pf) {
+        case 2: return launch_gemv_kp<K, 2>(p, s);
+        case 4: return launch_gemv_kp<K, 4>(p, s);
+        case 8: return launch_gemv_kp<K, 8>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int K, const GemvParams& p, hipStream_t s) {
+    switch (K) {
+        case 1: return launch_gemv_k<1>(p, s);
+        case 2: return launch_gemv_k<2>(p, s);
+        case 3: return launch_gemv_k<3>(p, s);
+        case 4: return launch_gemv_k<4>(p, s);
+        case 5: return launch_gemv_k<5>(p, s);
+        case 6: return launch_gemv_k<6>(p, s);
+        case 7: return launch_gemv_k<7>(p, s);
+        case 8: return launch_gemv_k<8>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace exl3

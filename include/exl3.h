@@ -1,0 +1,122 @@
+/*
+ * exl3.h - C ABI of the EXL3 trellis decode-matmul library for MI355X (gfx950).
+ *
+ * The operation (pages: "ExLlamaV3 inference speed: EXL3 GEMM kernel and fused
+ * Viterbi encoding", sections "GEMM kernel", "small-batch GEMV" and "Viterbi
+ * encoding kernel"; "ExLlamaV3 overview", section "EXL3 format"):
+ *
+ *     y[r][o] = out_scale[o] * sum_k x'[r][k] * W[o][k],
+ *     x'[r]   = blockdiag(H128) (sign * x[r])       (Hadamard rotation of the input)
+ *
+ * W is never stored: each 16x16 tile of W is a tail-biting bitshift trellis
+ * stream of 256*K bits (K bits per weight), packed into 16*K little-endian
+ * uint16 words and decoded on the fly by a table-free codebook.
+ *
+ * Format (the pages leave these open; this library fixes them):
+ *   - W is [n_out][n_in] (y = x' W^T).  Tile (tr, tc) covers rows 16tr..16tr+15
+ *     and columns 16tc..16tc+15.  trellis[tr][tc][w], w < 16K, so one 16-row
+ *     strip (fixed tr) is contiguous.  Tile element i is W[16tr + i/16][16tc + i%16].
+ *   - Stream bit j of a tile is bit (j % 16) of word j / 16.  State
+ *     s_i = bits [iK, iK+16) of the stream, taken cyclically (i = 0..255).
+ *   - Codebook: p = s*0xBFD3 + 0x201784FF (mod 2^32); q = (p & 0x8D7F8DFF) | 0x30003000;
+ *     the value is the fp16 sum, rounded to nearest even, of q's two fp16 halves.
+ *   - H128 is the unnormalised 128x128 Sylvester matrix, H[i][j] = (-1)^popcount(i&j),
+ *     applied to each block of 128 consecutive input features.
+ *   - fp16 values travel as uint16_t bit patterns.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers owned by the caller; the library allocates
+ *     nothing and keeps no per-call state.  Tensors are contiguous, row-major,
+ *     and at least 16-byte aligned.  x and y must not alias.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous: argument errors are returned synchronously, before any
+ *     launch; launch failures are reported as EXL3_EHIP from hipGetLastError
+ *     right after the launch; device faults surface at the caller's next
+ *     synchronisation.
+ *   - No C++ exception crosses this interface.  Calls on different streams
+ *     may run concurrently if each has its own workspace.
+ */
+#ifndef EXL3_H
+#define EXL3_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum exl3_status {
+    EXL3_OK = 0,
+    EXL3_EINVAL = -1,       /* null pointer, bad shape, bad bit width, bad m        */
+    EXL3_EUNSUPPORTED = -2, /* valid request that this build cannot serve           */
+    EXL3_EWORKSPACE = -3,   /* workspace missing or smaller than exl3_pack_info says */
+    EXL3_EHIP = -4          /* a HIP runtime call or a kernel launch failed          */
+};
+
+typedef struct exl3_pack_info_t {
+    int32_t n_in, n_out, bits, max_m; /* echo of the arguments                        */
+    int32_t tiles_in, tiles_out;      /* n_in / 16, n_out / 16                         */
+    int32_t words_per_tile;           /* 16 * bits                                     */
+    int32_t reserved;
+    int64_t trellis_words;            /* tiles_in * tiles_out * words_per_tile         */
+    int64_t trellis_bytes;            /* n_in * n_out * bits / 8                       */
+    int64_t workspace_bytes;          /* enough for exl3_gemv and exl3_gemm, any m <= max_m */
+} exl3_pack_info_t;
+
+/*
+ * exl3_pack_info: sizes of the packed weight and of the workspace.
+ *   n_in % 128 == 0, n_out % 16 == 0, 1 <= bits <= 8, max_m >= 1.
+ * Host-only; never touches the GPU.  Returns EXL3_EINVAL on bad arguments.
+ */
+int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m,
+                   exl3_pack_info_t* out);
+
+/*
+ * exl3_decode_tile: decode n_tiles packed tiles (pages: "Viterbi encoding
+ * kernel" packs each 16x16 block as a 16-bit index sequence; "GEMM kernel"
+ * turns an index into a half with a multiply and a bit operation).
+ *   words : uint16 [n_tiles][16*bits], device.
+ *   out   : fp16 bits [n_tiles][256], device; element i of tile t at out[256t + i]
+ *           (trellis order = row-major over the 16x16 tile).  Bit-exact.
+ * n_tiles == 0 is a no-op.  EXL3_EINVAL for null pointers, n_tiles < 0 or a bad
+ * bit width.
+ */
+int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
+                     uint16_t* out, void* stream);
+
+/*
+ * exl3_gemv: the decode-matmul for 1 <= m <= 8 (pages: "small-batch GEMV",
+ * where small m makes the weight stream the bottleneck).
+ *   x         : fp16 [m][n_in]
+ *   trellis   : uint16 [n_out/16][n_in/16][16*bits]
+ *   sign      : fp16 [n_in], entries +-1
+ *   out_scale : fp16 [n_out]
+ *   y         : fp16 [m][n_out] (overwritten; fp32 accumulation, round to nearest even)
+ *   workspace : device scratch of at least exl3_pack_info(...).workspace_bytes
+ *               bytes for max_m >= m.  Its contents need no initialisation and
+ *               are meaningless after the call.  Calls that may run at the same
+ *               time (different streams) need separate workspaces.
+ * m == 0 is a no-op.  m > 8 or m < 0 gives EXL3_EINVAL (use exl3_gemm).
+ */
+int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+              const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
+              uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * exl3_gemm: the same result for any m >= 1, built for m >= 16 (pages: "GEMM
+ * kernel", where the Hadamard rotation of the input and the decode are fused
+ * with a tiled matrix product).  Arguments and workspace rules as exl3_gemv.
+ */
+int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+              const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
+              uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text for a status code (static storage; never NULL). */
+const char* exl3_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXL3_H */

@@ -55,6 +55,12 @@ def draw(mm: Matmul, with_words: bool = True):
     return words, x, sign, out_scale
 
 
+def words_only(n_in: int, n_out: int, K: int, seed) -> np.ndarray:
+    """Packed words alone (first draw of the recipe) for an extra weight matrix."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(0, 65536, size=(n_out // 16, n_in // 16, 16 * K), dtype=np.uint16)
+
+
 def random_case(n_in: int, n_out: int, K: int, m: int, seed) -> tuple:
     """Arbitrary-shape case with the same recipe (used for small parity shapes)."""
     return draw(Matmul("case", n_in, n_out, K, m, seed))

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI: the library loads, exports what the header
+declares, sizes packed weights and workspaces, and rejects bad arguments before
+touching the GPU.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_gemm_exl3_amd as ex
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "exl3.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(exl3_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ex.lib_path()):
+        pytest.fail("libexl3.so is not built (run __graft_entry__.build())")
+    return ex.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemm",
+                          "exl3_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_pack_info_sizes(lib):
+    for n_in, n_out, K, mm in [(4096, 4096, 4, 1), (14336, 4096, 3, 8), (8192, 28672, 2, 2048), (128, 16, 1, 1)]:
+        info = ex.pack_info(n_in, n_out, K, mm)
+        assert info["tiles_in"] == n_in // 16 and info["tiles_out"] == n_out // 16
+        assert info["words_per_tile"] == 16 * K
+        assert info["trellis_words"] == (n_in // 16) * (n_out // 16) * 16 * K
+        assert info["trellis_bytes"] == n_in * n_out * K // 8 == 2 * info["trellis_words"]
+        assert info["workspace_bytes"] >= mm * n_in * 2              # gemm: rotated input
+    assert ex.pack_info(4096, 4096, 4, 1)["workspace_bytes"] < ex.pack_info(4096, 4096, 4, 64)["workspace_bytes"]
+
+
+@pytest.mark.parametrize("args", [(100, 16, 4, 1), (128, 17, 4, 1), (128, 16, 0, 1), (128, 16, 9, 1),
+                                  (128, 16, 4, 0), (0, 16, 4, 1), (-128, 16, 4, 1)])
+def test_pack_info_rejects(lib, args):
+    info = ex._PackInfo()
+    assert lib.exl3_pack_info(*args, ctypes.byref(info)) == -1
+    assert lib.exl3_pack_info(128, 16, 4, 1, None) == -1
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        s = ex.status_string(code)
+        assert isinstance(s, str) and s
+    assert ex.status_string(-3).startswith("workspace")
+
+
+def _gemv_call(lib, fn, x=1, m=1, tr=1, sg=1, sc=1, n_in=128, n_out=16, bits=4, y=2, ws=3, wsb=1 << 30):
+    return getattr(lib, fn)(x, m, tr, sg, sc, n_in, n_out, bits, y, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["exl3_gemv", "exl3_gemm"])
+def test_linear_argument_errors_return_before_launch(lib, fn):
+    # every case is rejected on the host, so fake non-null pointers are never used
+    assert _gemv_call(lib, fn, m=-1) == -1
+    assert _gemv_call(lib, fn, n_in=100) == -1
+    assert _gemv_call(lib, fn, n_out=24) == -1
+    assert _gemv_call(lib, fn, bits=0) == -1
+    assert _gemv_call(lib, fn, bits=9) == -1
+    assert _gemv_call(lib, fn, x=None) == -1
+    assert _gemv_call(lib, fn, tr=None) == -1
+    assert _gemv_call(lib, fn, sg=None) == -1
+    assert _gemv_call(lib, fn, sc=None) == -1
+    assert _gemv_call(lib, fn, y=None) == -1
+    assert _gemv_call(lib, fn, x=5, y=5) == -1          # aliasing
+    assert _gemv_call(lib, fn, m=0, x=None, y=None) == 0  # m == 0 is a no-op
+    # weights of 2 GiB or more are refused (32-bit buffer offsets)
+    assert _gemv_call(lib, fn, n_in=65536, n_out=65536, bits=4) == -2
+
+
+def test_gemm_workspace_errors(lib):
+    # gemm stages the rotated input in the workspace; gemv needs none
+    assert _gemv_call(lib, "exl3_gemm", ws=None) == -3
+    assert _gemv_call(lib, "exl3_gemm", wsb=16) == -3
+
+
+def test_gemv_rejects_m_above_8(lib):
+    assert _gemv_call(lib, "exl3_gemv", m=9) == -1
+
+
+def test_decode_tile_argument_errors(lib):
+    assert lib.exl3_decode_tile(1, 0, 1, 2, None) == -1
+    assert lib.exl3_decode_tile(1, 9, 1, 2, None) == -1
+    assert lib.exl3_decode_tile(1, 4, -1, 2, None) == -1
+    assert lib.exl3_decode_tile(None, 4, 1, 2, None) == -1
+    assert lib.exl3_decode_tile(1, 4, 1, None, None) == -1
+    assert lib.exl3_decode_tile(None, 4, 0, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setenv("EXL3_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ex, "_LIB", None)
+    with pytest.raises(ex.Exl3Error):
+        ex.load()

@@ -1,0 +1,243 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+decode_tile must match bit for bit; gemv / gemm must be within a relative
+Frobenius error of 1e-3 of the float64 oracle.  Every input comes from the
+seeded generators in `synth`; every expected value from `oracle`.
+"""
+import numpy as np
+import pytest
+
+import synth
+from oracle import exl3_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_gemm_exl3_amd as ex
+    ex.load()
+    return torch
+
+
+def log(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def to_dev(torch, a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).cuda()
+
+
+def rel_fro(y, ref):
+    y = np.asarray(y, np.float64)
+    return float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def run_linear(torch, fn, words, x, sign, scale, K, ws=None):
+    import decode_gemm_exl3_amd as ex
+    y = getattr(ex, fn)(to_dev(torch, x), to_dev(torch, words), to_dev(torch, sign), to_dev(torch, scale), K,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# --------------------------------------------------------------- decode -----
+def decode_gpu(torch, words, K):
+    import decode_gemm_exl3_amd as ex
+    w = to_dev(torch, words.reshape(-1, 16 * K))
+    out = ex.decode_tile(w, K)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("K", range(1, 9))
+def test_decode_random_tiles_bit_exact(torch_cuda, K):
+    log(f"decode random K={K}")
+    rng = np.random.default_rng(1000 + K)
+    for T in (1, 3, 4, 17, 1000):  # ragged tile counts
+        words = rng.integers(0, 65536, (T, 16 * K), dtype=np.uint16)
+        got = decode_gpu(torch_cuda, words, K)
+        ref = O.fp16_bits(O.decode_tiles(words, K))
+        assert np.array_equal(got, ref), (K, T, np.argwhere(got != ref)[:5])
+
+
+@pytest.mark.parametrize("K", range(1, 9))
+def test_decode_structured_streams(torch_cuda, K):
+    log(f"decode structured K={K}")
+    nbits = 256 * K
+    tiles = [np.zeros(16 * K, np.uint16), np.full(16 * K, 0xFFFF, np.uint16),
+             np.full(16 * K, 0xA5C3, np.uint16), np.full(16 * K, 0x0001, np.uint16)]
+    for p in list(range(0, 40)) + [nbits - 20, nbits - 16, nbits - 1] + list(range(16 * K - 8, 16 * K + 8)):
+        w = np.zeros(16 * K, np.uint16)
+        w[(p % nbits) // 16] = 1 << (p % 16)
+        tiles.append(w)
+    words = np.stack(tiles)
+    got = decode_gpu(torch_cuda, words, K)
+    ref = O.fp16_bits(O.decode_tiles(words, K))
+    assert np.array_equal(got, ref)
+    assert (got[0] == 0xB1E7).all() and (got[1] == 0xBEB4).all()
+
+
+def test_decode_all_states_k8(torch_cuda):
+    # at K=8, state i = byte_i | byte_{i+1} << 8: tiles of bytes (a, b0, a, b1, ...)
+    # visit every (lo, hi) byte pair, i.e. all 65536 states, in 512 tiles
+    log("decode all states K=8")
+    tiles = []
+    for a in range(256):
+        for half in range(2):
+            bts = np.zeros(256, np.uint8)
+            bts[0::2] = a
+            bts[1::2] = np.arange(128) + 128 * half
+            tiles.append(bts.view(np.uint16))
+    words = np.stack(tiles)
+    st = O.tile_states(words, 8)
+    assert len(np.unique(st)) == 65536
+    got = decode_gpu(torch_cuda, words, 8)
+    assert np.array_equal(got, O.fp16_bits(O.decode_tiles(words, 8)))
+
+
+def test_decode_deterministic(torch_cuda):
+    rng = np.random.default_rng(3)
+    words = rng.integers(0, 65536, (4096, 48), dtype=np.uint16)
+    a = decode_gpu(torch_cuda, words, 3)
+    b = decode_gpu(torch_cuda, words, 3)
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------------- gemv -----
+TINY = [(128, 16), (128, 32), (256, 48), (384, 272), (1024, 1040)]
+
+
+@pytest.mark.parametrize("K", range(1, 9))
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+def test_linear_small_shapes(torch_cuda, fn, K):
+    for (n_in, n_out) in TINY:
+        for m in ((1, 2, 3, 4, 5, 8) if fn == "gemv" else (1, 7, 16, 33)):
+            log(f"{fn} K={K} n_in={n_in} n_out={n_out} m={m}")
+            words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [7, K, n_in, n_out, m])
+            ref = O.linear(x, words, sign, scale, K)
+            y = run_linear(torch_cuda, fn, words, x, sign, scale, K)
+            assert np.isfinite(y).all()
+            err = rel_fro(y, ref)
+            assert err <= TOL, (fn, K, n_in, n_out, m, err)
+
+
+def test_gemv_split_and_ragged(torch_cuda):
+    # many k chunks (arrival counters in play) and a strip count that is not a
+    # multiple of the per-workgroup strip block
+    import decode_gemm_exl3_amd as ex
+    for (n_in, n_out, K, m) in [(4096, 1040, 3, 1), (2048, 4112, 2, 6), (14336, 256, 4, 8), (8192, 48, 5, 3)]:
+        log(f"gemv split n_in={n_in} n_out={n_out} K={K} m={m}")
+        words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [8, n_in, n_out, K, m])
+        ref = O.linear(x, words, sign, scale, K)
+        ws = ex.Workspace(n_in, n_out, K, 8)
+        for rep in range(2):  # the same workspace twice in a row
+            y = run_linear(torch_cuda, "gemv", words, x, sign, scale, K, ws=ws)
+            assert rel_fro(y, ref) <= TOL, (n_in, n_out, K, m, rep)
+
+
+def test_workspace_reuse_across_shapes_and_m(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    ws = ex.Workspace(4096, 4096, 8, 64)
+    torch = torch_cuda
+    for (fn, m, K) in [("gemm", 40, 3), ("gemv", 8, 4), ("gemv", 1, 2), ("gemm", 3, 5), ("gemv", 5, 3)]:
+        log(f"reuse {fn} m={m} K={K}")
+        words, x, sign, scale = synth.random_case(4096, 4096, K, m, [9, m, K])
+        ref = O.linear(x, words, sign, scale, K)
+        y = run_linear(torch, fn, words, x, sign, scale, K, ws=ws)
+        assert rel_fro(y, ref) <= TOL, (fn, m, K)
+    # a workspace full of garbage must not matter
+    ws.buf.fill_(0xA5)
+    words, x, sign, scale = synth.random_case(4096, 4096, 3, 2, [9, 2, 3])
+    y = run_linear(torch, "gemv", words, x, sign, scale, 3, ws=ws)
+    assert rel_fro(y, O.linear(x, words, sign, scale, 3)) <= TOL
+
+
+def test_gemv_gemm_agree_and_deterministic(torch_cuda):
+    words, x, sign, scale = synth.random_case(2048, 1024, 4, 4, 77)
+    ref = O.linear(x, words, sign, scale, 4)
+    y1 = run_linear(torch_cuda, "gemv", words, x, sign, scale, 4)
+    y2 = run_linear(torch_cuda, "gemv", words, x, sign, scale, 4)
+    y3 = run_linear(torch_cuda, "gemm", words, x, sign, scale, 4)
+    assert rel_fro(y1, ref) <= TOL and rel_fro(y3, ref) <= TOL
+    assert rel_fro(y1.astype(np.float64), y3.astype(np.float64)) <= 2 * TOL
+    # fp32 atomics may reorder the split-k sum: allow last-bit differences only
+    assert np.abs(y1.astype(np.float64) - y2.astype(np.float64)).max() <= 2e-3 * np.abs(ref).max()
+
+
+def test_zero_m_is_noop(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    torch = torch_cuda
+    words, x, sign, scale = synth.random_case(128, 16, 2, 1, 1)
+    y = torch.full((0, 16), 7, dtype=torch.float16, device="cuda")
+    ex.gemv(to_dev(torch, x[:0]), to_dev(torch, words), to_dev(torch, sign), to_dev(torch, scale), 2, y=y)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------ the named workloads -----
+def sampled_rows(n_out, rng, k=48):
+    rows = np.concatenate([np.arange(16), n_out - 16 + np.arange(16), rng.integers(0, n_out, k)])
+    return np.unique(rows)
+
+
+def check_workload(torch, mm, fn, ws):
+    log(f"{fn} {mm.name} n_in={mm.n_in} n_out={mm.n_out} K={mm.K} m={mm.m}")
+    words, x, sign, scale = synth.draw(mm)
+    y = run_linear(torch, fn, words, x, sign, scale, mm.K, ws=ws)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(1)
+    rows = sampled_rows(mm.n_out, rng)
+    ref = O.linear_rows(x, words, sign, scale, mm.K, rows)
+    err = rel_fro(y[:, rows], ref)
+    assert err <= TOL, (mm.name, err)
+    return y
+
+
+def test_workload_single_layer_full(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    mm = synth.single_layer()[0]
+    words, x, sign, scale = synth.draw(mm)
+    log("single 4096x4096 K=4 full oracle")
+    ref = O.linear(x, words, sign, scale, mm.K)
+    ws = ex.Workspace(mm.n_in, mm.n_out, mm.K, 1)
+    y = run_linear(torch_cuda, "gemv", words, x, sign, scale, mm.K, ws=ws)
+    assert rel_fro(y, ref) <= TOL
+    y2 = run_linear(torch_cuda, "gemm", words, x, sign, scale, mm.K, ws=ws)
+    assert rel_fro(y2, ref) <= TOL
+
+
+def test_workload_llama8b_mlp(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    ws = ex.Workspace(14336, 14336, 8, 8)
+    for mm in synth.llama8b_mlp():
+        check_workload(torch_cuda, mm, "gemv", ws)
+
+
+def test_workload_llama70b_decode(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    ws = ex.Workspace(28672, 28672, 8, 1)
+    for mm in synth.llama70b_decode():
+        check_workload(torch_cuda, mm, "gemv", ws)
+
+
+def test_workload_prefill_gemm(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    ws = ex.Workspace(8192, 28672, 8, 2048)
+    for mm in synth.prefill_gemm():
+        check_workload(torch_cuda, mm, "gemm", ws)
+
+
+def test_workload_stack_sampled_layers(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    ws = ex.Workspace(14336, 14336, 8, 1)
+    stack = synth.llama8b_stack()
+    for mm in stack[:7] + stack[-7:]:
+        check_workload(torch_cuda, mm, "gemv", ws)
