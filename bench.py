@@ -177,6 +177,52 @@ def cpu_baseline(strips=896):
                       f"{dt:.1f} s, numpy fp64, BLAS limited to 1 thread"}
 
 
+def kernel_sources_hash() -> str:
+    """Hash of the GEMV kernel sources: counter-derived traffic is valid only for them."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("exl3_device.hpp", "exl3_kernels.hip"):
+        with open(os.path.join(ROOT, "decode_gemm_exl3_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    profile (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
+    kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "gemv_k4_llama8b_mlp_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_hash") != kernel_sources_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def only_mode(what, steps, replicas):
+    """Short runs for the profiler: the dominant GEMV alone, or a plain copy."""
+    import torch
+    import decode_gemm_exl3_amd as ex
+    if what == "copy":
+        nbytes = 256 << 20
+        a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each": nbytes, "copies": steps}), flush=True)
+        return
+    cases, ws = build_mlp(torch, ex, 1, Ks=(4,), replicas=replicas)
+    for i in range(steps):
+        run_step(ex, cases, ws, i % replicas)
+    torch.cuda.synchronize()
+    print(json.dumps({"gemv_k4_launches": steps * len(cases),
+                      "bytes_per_launch": [c["bytes"] for c in cases]}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +231,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=7)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--only", choices=["gemv_k4", "copy"], help="profiling runs: one kernel family only")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -195,6 +242,9 @@ def main():
     import decode_gemm_exl3_amd as ex
     ex.load()
     torch.cuda.init()
+    if args.only:
+        only_mode(args.only, args.steps, args.replicas)
+        return
 
     cases, ws = build_mlp(torch, ex, 1, replicas=args.replicas)
     step_bytes = sum(c["bytes"] for c in cases)
@@ -236,9 +286,9 @@ def main():
         "config": {"workload": "llama3.1-8b-mlp-gemv: gate/up 4096->14336, down 14336->4096, "
                                "K in {2,3,4}, m=1, 9 GEMVs per step",
                    "m": 1, "bits": [2, 3, 4], "weight_replicas": args.replicas},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<K=4,GS=4>", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<K=4>", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": recorded_traffic()},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "extra": extra,
     }

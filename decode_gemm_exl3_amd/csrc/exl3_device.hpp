@@ -166,4 +166,54 @@ __device__ __forceinline__ void decode_row(const uint32_t (&b)[RowGeom<K>::NB], 
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Half rows, for the GEMM's matrix-core B operand (lane (n, g) holds 8
+// consecutive k of output n): half row h of row n = states 16n + 8h .. +7, the
+// bit window [8K(2n+h), 8K(2n+h) + 8K + 15) of the tile stream.  A lane loads
+// KDH dwords starting at the dword holding the window start, each with its own
+// (wrapped) offset, then shifts them so that state c starts at bit cK.
+// ---------------------------------------------------------------------------
+template <int K> struct HalfGeom {
+    static constexpr bool ALIGNED = (8 * K) % 32 == 0;  // window starts on a dword boundary
+    static constexpr int KDH = ALIGNED ? (8 * K + 15 + 31) / 32 : (24 + 8 * K + 15 + 31) / 32;
+};
+
+// Dword index (within the tile) of the i-th dword of half row h of row n, and
+// the bit offset of the window inside the first dword.
+template <int K>
+__device__ __forceinline__ uint32_t half_dword(int n, int h, int i) {
+    const int start = 8 * K * (2 * n + h);
+    return (uint32_t)(((start >> 5) + i) % (8 * K));
+}
+template <int K>
+__device__ __forceinline__ uint32_t half_shift(int n, int h) {
+    return (uint32_t)((8 * K * (2 * n + h)) & 31);
+}
+
+// Codebook words of the 8 states of a normalised half row (state c at bit cK).
+template <int K>
+__device__ __forceinline__ void decode_half(const uint32_t (&b)[HalfGeom<K>::KDH], uint32_t (&q)[8],
+                                            const CbRegs& r) {
+    constexpr int NB = HalfGeom<K>::KDH;
+    constexpr bool pairs = (16 % K) == 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int P = c * K;
+        const int dw = P >> 5;
+        const int sh = P & 31;
+        if (sh == 0) {
+            q[c] = cb_lo(b[dw], r);
+        } else if (sh == 16) {
+            q[c] = cb_hi(b[dw], r);
+        } else if (pairs && sh > 16 && c - 16 / K >= 0) {
+            // produced together with state c - 16/K
+        } else {
+            const uint32_t w = __builtin_amdgcn_alignbit(b[(dw + 1 < NB) ? dw + 1 : dw], b[dw], (uint32_t)sh);
+            q[c] = cb_lo(w, r);
+            if (pairs && c + 16 / K < 8) q[(c + 16 / K) & 7] = cb_hi(w, r);
+        }
+    }
+}
+
 }  // namespace exl3

@@ -1,100 +1,163 @@
 // exl3_gemm.hip - decode-matmul for larger m on the matrix cores (gfx950).
 //
-// The input is rotated once by a pre-pass (x'/128 in fp16, workspace).  Each
-// workgroup owns a BM x BN block of y and walks the input dimension in steps of
-// 64: it stages the x' block in LDS, decodes the 4 strips x 4 tiles of weights
-// it needs into LDS as fp16 (halves summed), and runs v_mfma_f32_16x16x32_f16.
+// The input is rotated once by a pre-pass (x'/128 in fp16, workspace).  A
+// workgroup (4 waves) owns a BM x BN = 128 x 256 block of y; wave w owns all 128
+// rows and outputs 64w..64w+63 (4 strips).  The input dimension is walked in
+// steps of BK = 64 (4 tile columns):
+//   - the x' block [128][64] is staged in LDS (loaded one step ahead into
+//     registers) and read as A fragments by all four waves;
+//   - each wave decodes its own weights straight into B fragments: lane (n, g)
+//     decodes half row g & 1 of row n of tile column g >> 1 (8 states, halves
+//     summed to fp16), so decoded weights never touch LDS and are decoded once
+//     per workgroup; the trellis rows are loaded one step ahead;
+//   - 8 x 4 fragments of v_mfma_f32_16x16x32_f16 per 32 inputs: 64 MFMAs per
+//     wave per step.
+// Within one wave the vector decode and the matrix core hardly overlap, but the
+// matrix core runs one wave's MFMAs while another wave on the same SIMD
+// decodes, so the kernel is sized for two workgroups per CU (at most 256
+// registers per lane, 128 of them accumulators) and keeps LDS traffic to x'.
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
 
 namespace exl3 {
 
-constexpr int GM_BM = 64;
-constexpr int GM_BN = 64;             // 4 strips
+constexpr int GM_BM = 128;
+constexpr int GM_BN = 256;            // 16 strips, 64 outputs per wave
 constexpr int GM_BK = 64;             // 4 tile columns
-constexpr int GM_LDA = GM_BK + 8;     // padded row stride in halves
+constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 bytes)
+constexpr int GM_A_HALVES = GM_BM * GM_LD;
 
 template <int K>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-    __shared__ __align__(16) uint16_t As[GM_BM * GM_LDA];
-    __shared__ __align__(16) uint16_t Bs[GM_BN * GM_LDA];
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmParams p) {
+    __shared__ __align__(16) uint16_t As[GM_A_HALVES];
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int n = lane & 15, g = lane >> 4;
-    const int m0 = blockIdx.y * GM_BM;
-    const int s0 = blockIdx.x * (GM_BN / 16);
-    const int wm = wave >> 1, wn = wave & 1;
+    // XCD-aware block order: consecutive workgroups go to different XCDs (round
+    // robin), so hand each XCD a contiguous run of the m-major block order; its
+    // L2 then keeps the x' rows of one m-block while it sweeps the outputs.
+    const int nbx = gridDim.x, total = gridDim.x * gridDim.y;
+    int lin = blockIdx.x + blockIdx.y * nbx;
+    if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+    const int m0 = (lin / nbx) * GM_BM;
+    const int s0 = (lin % nbx) * (GM_BN / 16) + 4 * wave;  // first strip of this wave
     const CbRegs cr = cb_regs();
 
-    f32x4_t acc[2][2];
+    // ---- weights: fragment f = (strip s0 + (f & 3), tile column 2(f >> 2) + (g >> 1), half g & 1).
+    // Lane offsets are fixed; strip and step go in the scalar offset.  Strips past
+    // the end read as zero (never written out).
+    constexpr int KDH = HalfGeom<K>::KDH;
+    constexpr uint32_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.trellis, (int64_t)p.n_strips * p.tiles_in * TILE_B);
+    const int h = g & 1;
+    uint32_t voff[KDH];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < KDH; ++i) voff[i] = (uint32_t)(g >> 1) * TILE_B + half_dword<K>(n, h, i) * 4;
+    const uint32_t bsh = half_shift<K>(n, h);
+    const uint32_t strip_b = (uint32_t)p.tiles_in * TILE_B;
+    auto load_frag = [&](uint32_t (&d)[KDH], int f, int tc) {
+        const uint32_t so = (uint32_t)(s0 + (f & 3)) * strip_b + (uint32_t)(tc + 2 * (f >> 2)) * TILE_B;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < KDH; ++i) d[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], so, kNT);
+    };
 
-    const int strip = s0 + wave;  // strip this wave decodes (past the end: reads zeros)
-    constexpr int64_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
-    const int64_t strip_off = (int64_t)strip * p.tiles_in * TILE_B;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(reinterpret_cast<const char*>(p.trellis) + strip_off,
-                                                (int64_t)p.n_strips * p.tiles_in * TILE_B - strip_off);
+    // ---- x' staging: thread t stages half (t & 1) of row t >> 1, 64 bytes per
+    // step.  Rows past m read as zero through the buffer range check.
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.xr + (int64_t)m0 * p.n_in, ((int64_t)p.m - m0) * p.n_in * 2);
+    const int arow = tid >> 1, acol = (tid & 1) * 32;  // in halves
+    const uint32_t aoff = (uint32_t)arow * p.n_in * 2 + acol * 2;
+
+    // trellis rows one step in flight: each fragment's registers are refilled
+    // with the same fragment of the next step as soon as they are decoded
+    uint32_t rows[8][KDH];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) load_frag(rows[f], f, 0);
+    u32x4_t areg[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        areg[c] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, (8 * c) * 2, 0));
+
+    f32x4_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
     for (int tc = 0; tc < p.tiles_in; tc += 4) {
-        // stage x' rows m0..m0+63, inputs 16tc..16tc+63
-        for (int e = tid; e < GM_BM * (GM_BK / 8); e += 256) {
-            const int r = e / (GM_BK / 8), cc = (e % (GM_BK / 8)) * 8;
-            u32x4_t v = {0u, 0u, 0u, 0u};
-            if (m0 + r < p.m)
-                v = *reinterpret_cast<const u32x4_t*>(p.xr + (int64_t)(m0 + r) * p.n_in + tc * 16 + cc);
-            *reinterpret_cast<u32x4_t*>(As + r * GM_LDA + cc) = v;
-        }
-        // decode strip `wave`, tile column tc + g, row n
-        uint32_t b[RowGeom<K>::NB];
-        load_row<K>(rs, (uint32_t)((tc + g) * (RowGeom<K>::DW_PER_TILE * 4)) + row_offset<K>(n), 0u, b);
-        finish_row<K>(n, b);
-        uint32_t q[16];
-        decode_row<K>(b, q, cr);
-        uint32_t o[8];
+        {
+            __syncthreads();  // the previous step's A fragments have been read
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = (uint32_t)cb_sum(q[2 * j]) | ((uint32_t)cb_sum(q[2 * j + 1]) << 16);
-        u32x4_t* dst = reinterpret_cast<u32x4_t*>(Bs + (wave * 16 + n) * GM_LDA + g * 16);
-        dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
-        dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
-        __syncthreads();
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4_t*>(As + arow * GM_LD + acol + 8 * c) = areg[c];
 #pragma unroll
-        for (int kk = 0; kk < GM_BK; kk += 32) {
-            half8_t af[2], bf[2];
+            for (int c = 0; c < 4; ++c)  // next step (past the end: range check or unused)
+                areg[c] = __builtin_bit_cast(u32x4_t,
+                                             __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, ((tc + 4) * 16 + 8 * c) * 2, 0));
+            __syncthreads();
+            const uint16_t* ab = As;
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = *reinterpret_cast<const half8_t*>(As + (wm * 32 + i * 16 + n) * GM_LDA + kk + 8 * g);
+            for (int kk = 0; kk < 2; ++kk) {
+                // decode the 4 B fragments of these 32 inputs, refilling each slot
+                // with the same fragment of the next step
+                half8_t bf[4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bf[j] = *reinterpret_cast<const half8_t*>(Bs + (wn * 32 + j * 16 + n) * GM_LDA + kk + 8 * g);
+                for (int j = 0; j < 4; ++j) {
+                    const int f = 4 * kk + j;
+                    uint32_t d[KDH];
+                    if constexpr (HalfGeom<K>::ALIGNED) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                        for (int i = 0; i < KDH; ++i) d[i] = rows[f][i];
+                    } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        __syncthreads();
-    }
-    // D[4g + r][n] of fragment (i, j)
+                        for (int i = 0; i < KDH; ++i)
+                            d[i] = __builtin_amdgcn_alignbit(rows[f][i + 1 < KDH ? i + 1 : i], rows[f][i], bsh);
+                    }
+                    load_frag(rows[f], f, tc + 4);
+                    uint32_t q[8];
+                    decode_half<K>(d, q, cr);
+                    uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = (uint32_t)cb_sum(q[2 * e]) | ((uint32_t)cb_sum(q[2 * e + 1]) << 16);
+                    bf[j] = __builtin_bit_cast(half8_t, u32x4_t{o[0], o[1], o[2], o[3]});
+                }
+                // A fragments through a ring of 3: reads run two fragments ahead
+                // of the 4 MFMAs that use each one
+                const uint16_t* abase = ab + n * GM_LD + 32 * kk + 8 * g;
+                half8_t af[3];
+                af[0] = *reinterpret_cast<const half8_t*>(abase);
+                af[1] = *reinterpret_cast<const half8_t*>(abase + 16 * GM_LD);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int o = (s0 * 16) + wn * 32 + j * 16 + n;
-            if (o >= p.n_out) continue;
-            const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
+                for (int i = 0; i < 8; ++i) {
+                    if (i + 2 < 8) af[(i + 2) % 3] = *reinterpret_cast<const half8_t*>(abase + (i + 2) * 16 * GM_LD);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * 32 + i * 16 + 4 * g + r;
-                if (row < p.m) p.y[(int64_t)row * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * acc[i][j][r]));
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i % 3], bf[j], acc[i][j], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
+    }
+    // D[4g + r][n] of fragment (i, j): row 16i + 4g + r, output 16 (s0 + j) + n
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int o = (s0 + j) * 16 + n;
+        if (o >= p.n_out) continue;
+        const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + i * 16 + 4 * g + r;
+                if (row < p.m) p.y[(int64_t)row * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * acc[i][j][r]));
+            }
+    }
 }
 
 template <int K>
 static hipError_t launch_gemm_k(const GemmParams& p, hipStream_t s) {
-    dim3 grid((p.n_strips + 3) / 4, (p.m + GM_BM - 1) / GM_BM);
+    dim3 grid((p.n_strips + 15) / 16, (p.m + GM_BM - 1) / GM_BM);
     hipLaunchKernelGGL(gemm_kernel<K>, grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
