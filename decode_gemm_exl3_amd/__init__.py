@@ -17,11 +17,12 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemm",
-           "status_string"]
+__all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemv_multi",
+           "gemm", "status_string", "MAX_PROJ"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
+MAX_PROJ = 4  # EXL3_GEMV_MAX_PROJ
 
 
 class Exl3Error(RuntimeError):
@@ -38,6 +39,11 @@ class _PackInfo(ctypes.Structure):
                 ("words_per_tile", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("trellis_words", ctypes.c_int64), ("trellis_bytes", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_int64)]
+
+
+class _Proj(ctypes.Structure):
+    _fields_ = [("trellis", ctypes.c_void_p), ("out_scale", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n_out", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def load() -> ctypes.CDLL:
@@ -58,6 +64,8 @@ def load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    lib.exl3_gemv_multi.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(_Proj), i32, vp, sz, vp]
+    lib.exl3_gemv_multi.restype = ctypes.c_int
     lib.exl3_status_string.argtypes = [ctypes.c_int]
     lib.exl3_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -133,6 +141,27 @@ def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=N
 def gemv(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
     """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 8 (fp16 out)."""
     return _linear("exl3_gemv", x, trellis, sign, out_scale, bits, workspace, y, stream)
+
+
+def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None):
+    """One launch for several projections of the same x (1 <= m <= 8).
+
+    weights: sequence of (trellis, out_scale) pairs sharing n_in and bits; the
+    same sign vector applies to all.  Returns the list of y, fp16 [m, n_out_i].
+    """
+    import torch
+    m, n_in = x.shape
+    n = len(weights)
+    if ys is None:
+        ys = [torch.empty((m, sc.shape[0]), dtype=torch.float16, device=x.device) for _, sc in weights]
+    arr = (_Proj * max(n, 1))()
+    for i, ((tr, sc), y) in enumerate(zip(weights, ys)):
+        arr[i] = _Proj(_ptr(tr), _ptr(sc), _ptr(y), int(sc.shape[0]), 0)
+    ws = 0 if workspace is None else _ptr(workspace.buf)
+    wsb = 0 if workspace is None else workspace.nbytes
+    rc = load().exl3_gemv_multi(_ptr(x), m, _ptr(sign), n_in, bits, arr, n, ws, wsb, _stream(stream))
+    _check(rc, "exl3_gemv_multi")
+    return ys
 
 
 def gemm(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):

@@ -1,5 +1,6 @@
 // exl3_api.hip - the C ABI: argument checks, workspace layout, dispatch.
 #include <atomic>
+#include <climits>
 #include <cstdlib>
 
 #include "../../include/exl3.h"
@@ -136,6 +137,54 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles, uint1
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
 }
 
+int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t n_in, int32_t bits,
+                    const exl3_proj_t* proj, int32_t n_proj, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (m < 0 || m > 8 || bits < 1 || bits > 8 || n_in <= 0 || (n_in % 128) != 0) return EXL3_EINVAL;
+    if (!proj || n_proj < 1 || n_proj > EXL3_GEMV_MAX_PROJ) return EXL3_EINVAL;
+    for (int i = 0; i < n_proj; ++i) {
+        const int32_t n_out = proj[i].n_out;
+        if (n_out <= 0 || (n_out % 16) != 0) return EXL3_EINVAL;
+    }
+    if (m == 0) return EXL3_OK;
+    if (!x || !sign) return EXL3_EINVAL;
+    int64_t strips = 0;
+    for (int i = 0; i < n_proj; ++i) {
+        const exl3_proj_t& q = proj[i];
+        if (!q.trellis || !q.out_scale || !q.y) return EXL3_EINVAL;
+        if ((const void*)q.y == (const void*)x) return EXL3_EINVAL;
+        for (int j = 0; j < i; ++j)
+            if (proj[j].y == q.y) return EXL3_EINVAL;
+        // weights are read through 32-bit buffer offsets
+        if ((int64_t)n_in * q.n_out * bits / 8 >= ((int64_t)1 << 31) - ((int64_t)1 << 20)) return EXL3_EUNSUPPORTED;
+        strips += q.n_out / 16;
+    }
+    if (strips > ((int64_t)1 << 30)) return EXL3_EUNSUPPORTED;
+    exl3::GemvParams p;
+    p.x = x;
+    p.sign = sign;
+    int end = 0;
+    for (int i = 0; i < exl3::GEMV_MAX_PROJ; ++i) {
+        const bool used = i < n_proj;
+        p.trellis[i] = used ? proj[i].trellis : nullptr;
+        p.out_scale[i] = used ? proj[i].out_scale : nullptr;
+        p.y[i] = used ? proj[i].y : nullptr;
+        p.n_out[i] = used ? proj[i].n_out : 0;
+        end += used ? proj[i].n_out / 16 : 0;
+        p.strip_end[i] = i < n_proj - 1 ? end : INT32_MAX;
+    }
+    p.n_proj = n_proj;
+    p.m = m;
+    p.n_in = n_in;
+    p.tiles_in = n_in / 16;
+    p.n_strips = (int)strips;
+    if (!plan_gemv(&p)) return EXL3_EUNSUPPORTED;
+    hipError_t e = exl3::launch_gemv(bits, p, (hipStream_t)stream);
+    return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+}
+
 int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
               void* workspace, size_t workspace_bytes, void* stream) {
@@ -144,20 +193,13 @@ int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
     int rc = common_checks(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes,
                            gemv_ws_bytes(n_out, mm));
     if (rc <= 0) return rc;
-    exl3::GemvParams p;
-    p.x = x;
-    p.trellis = trellis;
-    p.sign = sign;
-    p.out_scale = out_scale;
-    p.y = y;
-    p.m = m;
-    p.n_in = n_in;
-    p.n_out = n_out;
-    p.tiles_in = n_in / 16;
-    p.n_strips = n_out / 16;
-    if (!plan_gemv(&p)) return EXL3_EUNSUPPORTED;
-    hipError_t e = exl3::launch_gemv(bits, p, (hipStream_t)stream);
-    return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+    exl3_proj_t one;
+    one.trellis = trellis;
+    one.out_scale = out_scale;
+    one.y = y;
+    one.n_out = n_out;
+    one.reserved = 0;
+    return exl3_gemv_multi(x, m, sign, n_in, bits, &one, 1, workspace, workspace_bytes, stream);
 }
 
 int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,

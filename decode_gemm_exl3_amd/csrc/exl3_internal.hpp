@@ -7,14 +7,23 @@ namespace exl3 {
 
 constexpr int GEMV_LDS_BUDGET = 160 * 1024;  // bytes of LDS per GEMV workgroup (one per CU)
 
+constexpr int GEMV_MAX_PROJ = 4;  // projections sharing one input in one GEMV launch
+
+// One GEMV launch: up to GEMV_MAX_PROJ projections that share x, sign, n_in
+// and the bit width.  Their 16-row strips are numbered one after the other
+// (projection 0 first); strip_end[i] is the number of strips in projections
+// 0..i, and entries past the last projection hold INT32_MAX.
 struct GemvParams {
     const uint16_t* x;
-    const uint16_t* trellis;
     const uint16_t* sign;
-    const uint16_t* out_scale;
-    uint16_t* y;
-    int m, n_in, n_out;
-    int tiles_in, n_strips;
+    const uint16_t* trellis[GEMV_MAX_PROJ];
+    const uint16_t* out_scale[GEMV_MAX_PROJ];
+    uint16_t* y[GEMV_MAX_PROJ];
+    int n_out[GEMV_MAX_PROJ];
+    int strip_end[GEMV_MAX_PROJ];
+    int n_proj;
+    int m, n_in;
+    int tiles_in, n_strips;  // n_strips: all projections together
     int kc;             // tile columns per input chunk (x' of a chunk sits in LDS)
     int n_kchunks;      // input chunks
     int waves;          // waves per workgroup

@@ -1,4 +1,6 @@
 // exl3_kernels.hip - decode, input rotation and GEMV kernels for gfx950.
+#include <atomic>
+
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
 
@@ -136,6 +138,10 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict_
 // A step is one wave-wide load of 4 consecutive tiles of a strip (4 * 32K
 // contiguous bytes).
 //
+// One launch may serve several projections of the same input (x, sign, n_in
+// and K shared): their strips are numbered one after the other and handed out
+// as one list, so q/k/v or gate/up cost one launch and one rotation of x.
+//
 // Persistent workgroups: workgroup b owns strips b, b + G, b + 2G, ... (G =
 // grid size, about one workgroup per CU).  The input dimension is cut into
 // chunks whose rotated input fits in LDS (usually one chunk).  For each chunk
@@ -168,28 +174,41 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     uint32_t* zero = xs + M * xcols;
     float* red = reinterpret_cast<float*>(zero + PF * 64);
 
-    // Weight rows come through one buffer resource over the whole matrix: the
-    // per-step offset is a scalar, the lane offset fixed; reads past the end
-    // (prefetch after the last segment) return zero.
+    // Weight rows come through one buffer resource per projection: the per-step
+    // offset is a scalar, the lane offset fixed; reads past the end (prefetch
+    // after the last segment) return zero.
     constexpr uint32_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
     constexpr uint32_t STEP_B = 4 * TILE_B;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(p.trellis, (int64_t)p.n_strips * p.tiles_in * TILE_B);
     const uint32_t loff = (uint32_t)g * TILE_B + row_offset<K>(n);
     const int col0 = 4 * wave * nsw;  // first tile column of this wave inside a chunk
-    // byte offset of step 0 of segment q (chunk q / nj, strip b + (q % nj) * G)
-    auto seg_off = [&](int q) -> uint32_t {
-        if (q >= nseg) return 0x7FFFFFF0u;  // past the end: zeros
-        const int c = q / nj, j = q % nj;
-        return (uint32_t)(((int64_t)(b + j * G) * p.tiles_in + c * p.kc + col0) * TILE_B);
+    // projection of global strip s (uniform), and the strips before it
+    auto proj_of = [&](int s) -> int {
+        return (s >= p.strip_end[0]) + (s >= p.strip_end[1]) + (s >= p.strip_end[2]);
+    };
+    auto proj_begin = [&](int pi) -> int { return pi == 0 ? 0 : p.strip_end[pi - 1]; };
+    auto proj_rsrc = [&](int pi) {
+        return make_rsrc(p.trellis[pi], (int64_t)(p.n_out[pi] >> 4) * p.tiles_in * TILE_B);
+    };
+    // segment q = (chunk q / nj, strip b + (q % nj) * G): its projection's
+    // resource and the byte offset of its step 0
+    struct Seg {
+        __amdgpu_buffer_rsrc_t rs;
+        uint32_t off;
+    };
+    auto seg_at = [&](int q) -> Seg {
+        if (q >= nseg) return Seg{proj_rsrc(p.n_proj - 1), 0x7FFFFFF0u};  // past the end: zeros
+        const int c = q / nj, s = b + (q % nj) * G;
+        const int pi = proj_of(s);
+        const int ls = s - proj_begin(pi);
+        return Seg{proj_rsrc(pi), (uint32_t)(((int64_t)ls * p.tiles_in + c * p.kc + col0) * TILE_B)};
     };
 
     // ---- weight stream first --------------------------------------------------
     uint32_t buf[PF][RowGeom<K>::NB];
     {
-        const uint32_t o0 = seg_off(0);
+        const Seg s0 = seg_at(0);
 #pragma unroll
-        for (int u = 0; u < PF; ++u) load_row<K>(rs, loff, o0 + u * STEP_B, buf[u]);
+        for (int u = 0; u < PF; ++u) load_row<K>(s0.rs, loff, s0.off + u * STEP_B, buf[u]);
     }
     for (int i = tid; i < PF * 64; i += 64 * W) zero[i] = 0u;
     for (int i = tid; i < nj * W * M * 16; i += 64 * W) red[i] = 0.f;
@@ -239,14 +258,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
             // this segment's x' fragments: data lanes walk their row, others read zeros
             const uint32_t* ap = adata ? xs + n * xcols + wave * nsw * 64 + g * 16 : zero;
             const int astep = adata ? PF * 64 : 0;
-            const uint32_t cur = seg_off(q), nxt = seg_off(q + 1);
+            const Seg cur = seg_at(q), nxt = seg_at(q + 1);
             // one accumulator per MFMA of a step: no back-to-back dependent MFMAs
             f32x4_t acc[4];
 #pragma unroll
             for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             for (int st = 0; st < nsw; st += PF) {
                 // refills of this round target the next round: same segment or the next
-                const uint32_t roff = (st + PF < nsw) ? cur + (st + PF) * STEP_B : nxt;
+                const bool same = st + PF < nsw;
+                const uint32_t roff = same ? cur.off + (st + PF) * STEP_B : nxt.off;
+                const __amdgpu_buffer_rsrc_t rref = same ? cur.rs : nxt.rs;
 #pragma unroll
                 for (int u = 0; u < PF; ++u) {
                     // x' fragments first: their LDS latency hides behind the decode
@@ -259,7 +280,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                     uint32_t qq[16];
                     decode_row<K>(buf[u], qq, cr);
                     __builtin_amdgcn_sched_barrier(0);
-                    load_row<K>(rs, loff, roff + u * STEP_B, buf[u]);
+                    load_row<K>(rref, loff, roff + u * STEP_B, buf[u]);
                     // the refill stays here: the scheduler would otherwise sink the
                     // loads of the round to its end and expose the memory latency
                     __builtin_amdgcn_sched_barrier(0);
@@ -287,9 +308,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         const int j = idx / (M * 16), r = (idx >> 4) % M, cc = idx & 15;
         float v = 0.f;
         for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + r) * 16 + cc];
-        const int o = (b + j * G) * 16 + cc;
-        const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
-        p.y[(int64_t)r * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * v));
+        const int s = b + j * G, pi = proj_of(s);
+        const int o = (s - proj_begin(pi)) * 16 + cc;
+        const float sc = __half2float(__ushort_as_half(p.out_scale[pi][o])) * 128.0f;
+        p.y[pi][(int64_t)r * p.n_out[pi] + o] = __half_as_ushort(__float2half_rn(sc * v));
     }
 }
 
@@ -326,11 +348,16 @@ hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_i
 template <int K, int PF>
 static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
     const size_t lds = gemv_lds_bytes(p.m, p.waves, p.nsw, PF, (p.n_strips + p.grid - 1) / p.grid);
-    static bool attr_set = false;  // allow more than 64 KB of dynamic LDS
-    if (!attr_set) {
-        hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_BUDGET);
-        attr_set = true;
+    // allow more than 64 KB of dynamic LDS, once per device
+    static std::atomic<unsigned long long> attr_set{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (!(attr_set.load(std::memory_order_acquire) & bit)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_BUDGET);
+        if (e != hipSuccess) return e;
+        attr_set.fetch_or(bit, std::memory_order_release);
     }
     hipLaunchKernelGGL((gemv_kernel<K, PF>), dim3(p.grid), dim3(64 * p.waves), lds, s, p);
     return hipGetLastError();

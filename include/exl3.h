@@ -103,6 +103,37 @@ int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
               uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Most projections one exl3_gemv_multi call serves. */
+#define EXL3_GEMV_MAX_PROJ 4
+
+/* One projection of an exl3_gemv_multi call (host memory; read during the call only). */
+typedef struct exl3_proj_t {
+    const uint16_t* trellis;   /* uint16 [n_out/16][n_in/16][16*bits], device   */
+    const uint16_t* out_scale; /* fp16 [n_out], device                          */
+    uint16_t* y;               /* fp16 [m][n_out], device, overwritten          */
+    int32_t n_out;             /* n_out % 16 == 0                               */
+    int32_t reserved;          /* set to 0                                      */
+} exl3_proj_t;
+
+/*
+ * exl3_gemv_multi: exl3_gemv for up to EXL3_GEMV_MAX_PROJ projections of the
+ * same input in one launch, e.g. q/k/v or gate/up of a decoder layer (pages:
+ * "small-batch GEMV" for the path, and the summary's point that the kernels
+ * fuse work so that intermediate tensors and passes over memory disappear).
+ *   x, m, sign, n_in, bits : shared by every projection, as in exl3_gemv; the
+ *                            projections must have been quantised with the
+ *                            same input sign vector (one rotated input).
+ *   proj[0..n_proj-1]      : per projection trellis, out_scale, y and n_out.
+ *                            The y buffers must not overlap each other or x.
+ *   workspace              : as exl3_gemv (the GEMV needs none today).
+ * Each proj[i].y equals what exl3_gemv gives for that projection, up to fp32
+ * summation order.  m == 0 is a no-op.  EXL3_EINVAL for m outside 0..8, n_proj
+ * outside 1..EXL3_GEMV_MAX_PROJ, a null pointer, a bad shape or two identical y.
+ */
+int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t n_in, int32_t bits,
+                    const exl3_proj_t* proj, int32_t n_proj, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
 /*
  * exl3_gemm: the same result for any m >= 1, built for m >= 16 (pages: "GEMM
  * kernel", where the Hadamard rotation of the input and the decode are fused

@@ -116,3 +116,37 @@ def llama8b_stack(n_layers: int = 32) -> list[Matmul]:
             K = int(kb[b]) + (1 if attn else 0)
             out.append(Matmul(f"L{b}.{name}_k{K}", n_in, n_out, K, 1, [0, 5, 7 * b + j]))
     return out
+
+
+# --- projections fed by one input (one fused GEMV launch) ---------------------
+STACK_GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
+
+
+def llama8b_stack_groups(n_layers: int = 32) -> list[list[Matmul]]:
+    """The 224 stack matmuls grouped by the input they read: per layer q/k/v,
+    o, gate/up and down (128 groups).  Members keep their own seeds."""
+    by_name = {mm.name: mm for mm in llama8b_stack(n_layers)}
+    groups = []
+    for b in range(n_layers):
+        for _, members in STACK_GROUPS:
+            groups.append([next(v for k, v in by_name.items() if k.startswith(f"L{b}.{nm}_k"))
+                           for nm in members])
+    return groups
+
+
+def draw_group(mms: list[Matmul], with_words: bool = True):
+    """(words list, x, sign, out_scale list) for projections sharing one input.
+
+    Every member is drawn by `draw` with its own seed; the first member's x and
+    sign serve the whole group (one input, one rotation), the others' are
+    discarded.
+    """
+    words, scales = [], []
+    x = sign = None
+    for i, mm in enumerate(mms):
+        w, xi, si, sc = draw(mm, with_words)
+        words.append(w)
+        scales.append(sc)
+        if i == 0:
+            x, sign = xi, si
+    return words, x, sign, scales

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemm",
+    assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemv_multi", "exl3_gemm",
                           "exl3_status_string"}
     for n in names:
         assert hasattr(lib, n), n
@@ -91,6 +91,36 @@ def test_gemm_workspace_errors(lib):
 
 def test_gemv_rejects_m_above_8(lib):
     assert _gemv_call(lib, "exl3_gemv", m=9) == -1
+
+
+def _multi_call(lib, projs, x=1, m=1, sg=1, n_in=128, bits=4, n_proj=None):
+    arr = (ex._Proj * max(len(projs), 1))(*[ex._Proj(*p_) for p_ in projs])
+    return lib.exl3_gemv_multi(x, m, sg, n_in, bits, arr if projs else None,
+                               len(projs) if n_proj is None else n_proj, None, 0, None)
+
+
+def test_gemv_multi_argument_errors(lib):
+    # (trellis, out_scale, y, n_out, reserved); fake pointers, never dereferenced
+    good = [(11, 12, 13, 16, 0), (21, 22, 23, 32, 0)]
+    assert _multi_call(lib, good, m=-1) == -1
+    assert _multi_call(lib, good, m=9) == -1
+    assert _multi_call(lib, good, n_in=100) == -1
+    assert _multi_call(lib, good, bits=0) == -1
+    assert _multi_call(lib, good, bits=9) == -1
+    assert _multi_call(lib, [], n_proj=0) == -1
+    assert _multi_call(lib, good, n_proj=5) == -1
+    assert _multi_call(lib, good * 3) == -1                       # 6 > EXL3_GEMV_MAX_PROJ
+    assert _multi_call(lib, good, x=None) == -1
+    assert _multi_call(lib, good, sg=None) == -1
+    assert _multi_call(lib, [(0, 12, 13, 16, 0)]) == -1
+    assert _multi_call(lib, [(11, 0, 13, 16, 0)]) == -1
+    assert _multi_call(lib, [(11, 12, 0, 16, 0)]) == -1
+    assert _multi_call(lib, [(11, 12, 13, 24, 0)]) == -1          # n_out % 16
+    assert _multi_call(lib, [(11, 12, 13, 0, 0)]) == -1
+    assert _multi_call(lib, [(11, 12, 1, 16, 0)]) == -1           # y aliases x
+    assert _multi_call(lib, [(11, 12, 13, 16, 0), (21, 22, 13, 16, 0)]) == -1  # same y twice
+    assert _multi_call(lib, good, m=0, x=None, sg=None) == 0     # m == 0 is a no-op
+    assert _multi_call(lib, [(11, 12, 13, 65536, 0)], n_in=65536) == -2  # >= 2 GiB of weights
 
 
 def test_decode_tile_argument_errors(lib):

@@ -131,8 +131,8 @@ def test_linear_small_shapes(torch_cuda, fn, K):
 
 
 def test_gemv_split_and_ragged(torch_cuda):
-    # many k chunks (arrival counters in play) and a strip count that is not a
-    # multiple of the per-workgroup strip block
+    # long inputs (several LDS chunks at m = 8) and strip counts that leave the
+    # persistent workgroups with unequal strip counts
     import decode_gemm_exl3_amd as ex
     for (n_in, n_out, K, m) in [(4096, 1040, 3, 1), (2048, 4112, 2, 6), (14336, 256, 4, 8), (8192, 48, 5, 3)]:
         log(f"gemv split n_in={n_in} n_out={n_out} K={K} m={m}")
@@ -180,6 +180,62 @@ def test_zero_m_is_noop(torch_cuda):
     y = torch.full((0, 16), 7, dtype=torch.float16, device="cuda")
     ex.gemv(to_dev(torch, x[:0]), to_dev(torch, words), to_dev(torch, sign), to_dev(torch, scale), 2, y=y)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------- fused multi-projection GEMV -----
+def run_multi(torch, words, x, sign, scales, K):
+    import decode_gemm_exl3_amd as ex
+    ys = ex.gemv_multi(to_dev(torch, x), [(to_dev(torch, w), to_dev(torch, sc)) for w, sc in zip(words, scales)],
+                       to_dev(torch, sign), K)
+    torch.cuda.synchronize()
+    return [y.cpu().numpy() for y in ys]
+
+
+def group_case(n_in, n_outs, K, m, seed):
+    mms = [synth.Matmul(f"p{i}", n_in, n_out, K, m, [seed, i]) for i, n_out in enumerate(n_outs)]
+    return synth.draw_group(mms)
+
+
+@pytest.mark.parametrize("K", range(1, 9))
+def test_gemv_multi_small_shapes(torch_cuda, K):
+    for n_in, n_outs in [(128, (16,)), (256, (16, 48)), (512, (272, 16, 32)), (1024, (64, 1040, 16, 48))]:
+        for m in (1, 3, 8):
+            log(f"gemv_multi K={K} n_in={n_in} n_outs={n_outs} m={m}")
+            words, x, sign, scales = group_case(n_in, n_outs, K, m, 300 + K)
+            ys = run_multi(torch_cuda, words, x, sign, scales, K)
+            for i, (w, sc, y) in enumerate(zip(words, scales, ys)):
+                assert y.shape == (m, sc.shape[0])
+                err = rel_fro(y, O.linear(x, w, sign, sc, K))
+                assert err <= TOL, (K, n_in, n_outs, m, i, err)
+
+
+def test_gemv_multi_matches_separate_calls(torch_cuda):
+    # one launch over q/k/v-like and gate/up-like groups against one gemv per projection
+    for n_in, n_outs, K, m in [(4096, (4096, 1024, 1024), 5, 1), (4096, (14336, 14336), 3, 4)]:
+        log(f"gemv_multi vs gemv n_in={n_in} n_outs={n_outs} K={K} m={m}")
+        words, x, sign, scales = group_case(n_in, n_outs, K, m, 400)
+        ys = run_multi(torch_cuda, words, x, sign, scales, K)
+        rng = np.random.default_rng(2)
+        for w, sc, y in zip(words, scales, ys):
+            y1 = run_linear(torch_cuda, "gemv", w, x, sign, sc, K)
+            assert rel_fro(y.astype(np.float64), y1.astype(np.float64)) <= TOL
+            rows = sampled_rows(sc.shape[0], rng)
+            assert rel_fro(y[:, rows], O.linear_rows(x, w, sign, sc, K, rows)) <= TOL
+
+
+def test_gemv_multi_stack_layers(torch_cuda):
+    # first and last layer of the 32-layer stack, through the four fused groups
+    groups = synth.llama8b_stack_groups()
+    rng = np.random.default_rng(3)
+    for grp in groups[:4] + groups[-4:]:
+        log("gemv_multi stack " + "+".join(mm.name for mm in grp))
+        words, x, sign, scales = synth.draw_group(grp)
+        ys = run_multi(torch_cuda, words, x, sign, scales, grp[0].K)
+        for mm, w, sc, y in zip(grp, words, scales, ys):
+            assert np.isfinite(y).all()
+            rows = sampled_rows(mm.n_out, rng)
+            err = rel_fro(y[:, rows], O.linear_rows(x, w, sign, sc, mm.K, rows))
+            assert err <= TOL, (mm.name, err)
 
 
 # ------------------------------------------------ the named workloads -----
