@@ -186,21 +186,23 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         return (s >= p.strip_end[0]) + (s >= p.strip_end[1]) + (s >= p.strip_end[2]);
     };
     auto proj_begin = [&](int pi) -> int { return pi == 0 ? 0 : p.strip_end[pi - 1]; };
-    auto proj_rsrc = [&](int pi) {
-        return make_rsrc(p.trellis[pi], (int64_t)(p.n_out[pi] >> 4) * p.tiles_in * TILE_B);
-    };
     // segment q = (chunk q / nj, strip b + (q % nj) * G): its projection's
-    // resource and the byte offset of its step 0
+    // resource, the byte offset of its step 0 and the offset of the
+    // projection's last step.  Step offsets are clamped to that last step, so a
+    // wave's padding steps past the end of the last strip re-read real weights
+    // (they meet zero inputs) instead of leaving the buffer.
     struct Seg {
         __amdgpu_buffer_rsrc_t rs;
-        uint32_t off;
+        uint32_t off, lim;
     };
     auto seg_at = [&](int q) -> Seg {
-        if (q >= nseg) return Seg{proj_rsrc(p.n_proj - 1), 0x7FFFFFF0u};  // past the end: zeros
+        if (q >= nseg) return Seg{make_rsrc(p.trellis[0], 0), 0u, 0u};  // past the end: an empty buffer reads zeros
         const int c = q / nj, s = b + (q % nj) * G;
         const int pi = proj_of(s);
         const int ls = s - proj_begin(pi);
-        return Seg{proj_rsrc(pi), (uint32_t)(((int64_t)ls * p.tiles_in + c * p.kc + col0) * TILE_B)};
+        const int64_t bytes = (int64_t)(p.n_out[pi] >> 4) * p.tiles_in * TILE_B;
+        return Seg{make_rsrc(p.trellis[pi], bytes), (uint32_t)(((int64_t)ls * p.tiles_in + c * p.kc + col0) * TILE_B),
+                   (uint32_t)(bytes - STEP_B)};
     };
 
     // ---- weight stream first --------------------------------------------------
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     {
         const Seg s0 = seg_at(0);
 #pragma unroll
-        for (int u = 0; u < PF; ++u) load_row<K>(s0.rs, loff, s0.off + u * STEP_B, buf[u]);
+        for (int u = 0; u < PF; ++u) load_row<K>(s0.rs, loff, min(s0.off + u * STEP_B, s0.lim), buf[u]);
     }
     for (int i = tid; i < PF * 64; i += 64 * W) zero[i] = 0u;
     for (int i = tid; i < nj * W * M * 16; i += 64 * W) red[i] = 0.f;
@@ -267,6 +269,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                 // refills of this round target the next round: same segment or the next
                 const bool same = st + PF < nsw;
                 const uint32_t roff = same ? cur.off + (st + PF) * STEP_B : nxt.off;
+                const uint32_t rlim = same ? cur.lim : nxt.lim;
                 const __amdgpu_buffer_rsrc_t rref = same ? cur.rs : nxt.rs;
 #pragma unroll
                 for (int u = 0; u < PF; ++u) {
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                     uint32_t qq[16];
                     decode_row<K>(buf[u], qq, cr);
                     __builtin_amdgcn_sched_barrier(0);
-                    load_row<K>(rref, loff, roff + u * STEP_B, buf[u]);
+                    load_row<K>(rref, loff, min(roff + u * STEP_B, rlim), buf[u]);
                     // the refill stays here: the scheduler would otherwise sink the
                     // loads of the round to its end and expose the memory latency
                     __builtin_amdgcn_sched_barrier(0);
