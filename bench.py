@@ -130,26 +130,24 @@ def time_graphs(torch, ex, calls, replicas, steps, warmup, per_graph=1):
 
 
 def per_kernel_events(torch, ex, calls, replicas, steps):
-    """Average duration of each launch, from events recorded on the stream the
-    library launches on (the current stream)."""
+    """Average duration of each launch shape: HIP events on the stream the
+    library launches on (the current stream) around `steps` back-to-back
+    launches of that shape (weight replicas rotating), divided by `steps`."""
     stream = torch.cuda.current_stream()
     ev = []
     # a long GPU sleep first, so that every launch below is queued before the
     # GPU reaches it and the events time the GPU, not the host's launch rate
     torch.cuda._sleep(int(5e7))
-    for i in range(steps):
-        for c in calls:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+    for c in calls:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
             launch(ex, c, i % replicas)
-            b.record(stream)
-            ev.append((c["name"], a, b))
+        b.record(stream)
+        ev.append((c["name"], a, b))
     torch.cuda.synchronize()
-    dur = {}
-    for name, a, b in ev:
-        dur.setdefault(name, []).append(a.elapsed_time(b))
-    return {k: float(np.mean(v)) for k, v in dur.items()}
+    return {name: a.elapsed_time(b) / steps for name, a, b in ev}
 
 
 def copy_bandwidth(torch, nbytes=1 << 30, iters=10):
@@ -190,30 +188,37 @@ def gemm_tflops(torch, ex, iters=5):
     return 2.0 * m * n_in * n_out / (ms * 1e-3) / 1e12, ms
 
 
-def cpu_baseline(strips=896):
-    """CPU oracle on a bounded sample: gate 4096->14336 at K=4, m=1, `strips` 16-row strips."""
+def cpu_baseline():
+    """The CPU oracle on a bounded sample of the workload: the K=4 MLP at m=1
+    (gate and up 4096->14336, down 14336->4096), one BLAS thread."""
     import synth
     from oracle import exl3_oracle as O
     try:
         from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
         threadpool_limits = None
-    n_in, n_out, K, m = 4096, 14336, 4, 1
-    w = synth.words_only(n_in, n_out, K, [0, 2, K, 0])[:strips]
-    rng = np.random.default_rng([0, 2, K, 0, 1])
-    x = rng.standard_normal((m, n_in)).astype(np.float16)
-    sign = (2 * rng.integers(0, 2, n_in) - 1).astype(np.float16)
-    scale = (rng.uniform(0.5, 1.5, 16 * strips) * 0.02).astype(np.float16)
+    K, m = 4, 1
+    mats = [(nm, n_in, n_out, [0, 2, K, i]) for i, (nm, n_in, n_out) in
+            enumerate((("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)))]
+    inputs = []
+    for nm, n_in, n_out, seed in mats:
+        w = synth.words_only(n_in, n_out, K, seed)
+        rng = np.random.default_rng(seed + [1])
+        x = rng.standard_normal((m, n_in)).astype(np.float16)
+        sign = (2 * rng.integers(0, 2, n_in) - 1).astype(np.float16)
+        scale = (rng.uniform(0.5, 1.5, n_out) * 0.02).astype(np.float16)
+        inputs.append((w, x, sign, scale, gemv_bytes(n_in, n_out, K, m)))
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     t0 = time.perf_counter()
-    O.linear(x, w, sign, scale, K)
+    for w, x, sign, scale, _ in inputs:
+        O.linear(x, w, sign, scale, K)
     dt = time.perf_counter() - t0
-    if ctx is not None:
-        ctx.unregister() if hasattr(ctx, "unregister") else None
-    nbytes = gemv_bytes(n_in, 16 * strips, K, m)
+    if ctx is not None and hasattr(ctx, "unregister"):
+        ctx.unregister()
+    nbytes = sum(i[-1] for i in inputs)
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"gate 4096->{16 * strips} (first {strips} of 896 strips) K=4 m=1, "
-                      f"{dt:.1f} s, numpy fp64, BLAS limited to 1 thread"}
+            "sample": f"the K=4 MLP at m=1 (gate, up 4096->14336, down 14336->4096; 3 of the 9 projections "
+                      f"of a step), {dt:.1f} s, numpy fp64, BLAS limited to 1 thread"}
 
 
 def kernel_sources_hash() -> str:
