@@ -128,24 +128,19 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     // 32 inputs (k half kk) of a step: 8 row fragments x 4 output fragments;
     // the B fragments of k half kk were decoded by the wave with mh == kk
     auto mfma_half = [&](int buf, int kk) {
-        half8_t b[4];
+        // all 4 B and 8 A fragments of the half are read first: one LDS latency,
+        // then 32 back-to-back MFMAs
+        half8_t b[4], af[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(half8_t, Bs[buf][((kk * 4 + nq) * 4 + j) * 64 + lane]);
         const uint16_t* abase = &As[buf][(128 * mh + n) * GM_LD + 32 * kk + 8 * g];
-        // A fragments through a ring of 3: reads run two fragments ahead of the
-        // 4 MFMAs that use each one
-        half8_t af[3];
-        af[0] = *reinterpret_cast<const half8_t*>(abase);
-        af[1] = *reinterpret_cast<const half8_t*>(abase + 16 * GM_LD);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (i + 2 < 8) af[(i + 2) % 3] = *reinterpret_cast<const half8_t*>(abase + (i + 2) * 16 * GM_LD);
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const half8_t*>(abase + i * 16 * GM_LD);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i % 3], b[j], acc[i][j], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], b[j], acc[i][j], 0, 0, 0);
     };
 
     // ---- prologue: step 0 decoded and staged
