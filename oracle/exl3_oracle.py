@@ -37,6 +37,11 @@ FMT-6  H = 128x128 Sylvester matrix, H[i][j] = (-1)^popcount(i & j), unnormalise
 FMT-7  sign is +-1 per input feature, out_scale one fp16 per output feature.
 FMT-8  gemv: 1 <= m <= 8; gemm: any m >= 1.  Same result definition.
 FMT-9  K in 1..8.
+FMT-10 (the "dp4a" codebook the "GEMM kernel" section names as the alternative
+       to the multiply-and-lop3 one): p = (s*A' + B') mod 2^32; t = the sum of
+       p's four bytes (0..1020); c'(s) = RNE16((1024 + t) * G + C), one rounding,
+       with fp16 constants G = 1773/262144 (bits 0x1EED) and C = -10.375 (0xC930).
+       A' = 0xFEC5, B' = 0x77C40AA0.  Selected per call as codebook 1.
 
 The matrix product itself (FMT-1) has a plain definition, so the oracle is that
 definition evaluated in float64 after an exact decode.
@@ -55,6 +60,17 @@ CB_A = 0xBFD3
 CB_B = 0x201784FF
 CB_M = 0x8D7F8DFF
 CB_X = 0x30003000
+
+# FMT-10 constants (the byte-sum codebook).  Chosen by enumerating all 65536
+# states: A' odd and below 2^16; the byte sum of p has mean 510.009 and variance
+# 21835 (four independent uniform bytes: 510 and 21845); G and C are the fp16
+# pair that then gives mean 2e-4 and variance 0.9988; no result is subnormal.
+CB1_A = 0xFEC5
+CB1_B = 0x77C40AA0
+CB1_G = 0x1EED
+CB1_C = 0xC930
+
+CODEBOOKS = (0, 1)  # 0: multiply + mask-and-plant + half sum (FMT-5); 1: byte sum (FMT-10)
 
 TILE = 16
 TILE_ELEMS = 256
@@ -112,20 +128,39 @@ def codebook_halves(states: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return lo, hi
 
 
-def codebook(states: np.ndarray) -> np.ndarray:
-    """c(s) = RNE16(lo + hi) as float16 (FMT-5).
+def byte_sums(states: np.ndarray) -> np.ndarray:
+    """t(s) = sum of the four bytes of p = (s*A' + B') mod 2^32 (FMT-10), int64."""
+    s = np.asarray(states, dtype=np.uint64)
+    p = (s * np.uint64(CB1_A) + np.uint64(CB1_B)) & np.uint64(0xFFFFFFFF)
+    t = np.zeros(p.shape, dtype=np.uint64)
+    for k in range(4):
+        t += (p >> np.uint64(8 * k)) & np.uint64(0xFF)
+    return t.astype(np.int64)
 
-    The float32 sum of two fp16 values whose exponents differ by at most 3 is
-    exact, so casting it to float16 (NumPy rounds to nearest even) is one
-    correctly rounded fp16 addition.
+
+def codebook(states: np.ndarray, cb: int = 0) -> np.ndarray:
+    """The codebook value of each state as float16.
+
+    cb = 0 (FMT-5): c(s) = RNE16(lo + hi).  The float32 sum of two fp16 values
+    whose exponents differ by at most 3 is exact, so casting it to float16
+    (NumPy rounds to nearest even) is one correctly rounded fp16 addition.
+    cb = 1 (FMT-10): c'(s) = RNE16((1024 + t) * G + C).  With t < 2^10 and G, C
+    fp16, the float64 value is exact, so one cast is the single rounding.
     """
-    lo, hi = codebook_halves(states)
-    return (lo.astype(np.float32) + hi.astype(np.float32)).astype(np.float16)
+    if cb == 0:
+        lo, hi = codebook_halves(states)
+        return (lo.astype(np.float32) + hi.astype(np.float32)).astype(np.float16)
+    if cb == 1:
+        G = float(np.array([CB1_G], np.uint16).view(np.float16)[0])
+        C = float(np.array([CB1_C], np.uint16).view(np.float16)[0])
+        v = (1024.0 + byte_sums(states).astype(np.float64)) * G + C
+        return v.astype(np.float16)
+    raise ValueError(f"codebook must be one of {CODEBOOKS}, got {cb}")
 
 
-def decode_tiles(words: np.ndarray, K: int) -> np.ndarray:
+def decode_tiles(words: np.ndarray, K: int, cb: int = 0) -> np.ndarray:
     """Decode packed tiles to fp16 values in trellis order: [..., 16K] -> [..., 256]."""
-    return codebook(tile_states(words, K))
+    return codebook(tile_states(words, K), cb)
 
 
 # ---------------------------------------------------------------------------
@@ -138,9 +173,9 @@ def tiles_to_matrix(tiles: np.ndarray) -> np.ndarray:
     return tiles.reshape(to, ti, 16, 16).transpose(0, 2, 1, 3).reshape(to * 16, ti * 16)
 
 
-def dequant(trellis: np.ndarray, K: int) -> np.ndarray:
+def dequant(trellis: np.ndarray, K: int, cb: int = 0) -> np.ndarray:
     """Full fp16 weight matrix W [n_out, n_in] from trellis [n_out/16, n_in/16, 16K]."""
-    return tiles_to_matrix(decode_tiles(trellis, K))
+    return tiles_to_matrix(decode_tiles(trellis, K, cb))
 
 
 # ---------------------------------------------------------------------------
@@ -184,7 +219,7 @@ def _check_shapes(x, trellis, sign, out_scale, K):
     return m, n_in, to * 16
 
 
-def linear(x, trellis, sign, out_scale, K, strip_block: int = 64) -> np.ndarray:
+def linear(x, trellis, sign, out_scale, K, strip_block: int = 64, cb: int = 0) -> np.ndarray:
     """y = out_scale * (x' @ W^T) in float64 (FMT-1).
 
     x: fp16 [m, n_in]; trellis: uint16 [n_out/16, n_in/16, 16K];
@@ -196,12 +231,12 @@ def linear(x, trellis, sign, out_scale, K, strip_block: int = 64) -> np.ndarray:
     y = np.empty((m, n_out), dtype=np.float64)
     for t0 in range(0, n_out // 16, strip_block):
         t1 = min(n_out // 16, t0 + strip_block)
-        W = dequant(trellis[t0:t1], K).astype(np.float64)
+        W = dequant(trellis[t0:t1], K, cb).astype(np.float64)
         y[:, 16 * t0:16 * t1] = xr @ W.T
     return y * np.asarray(out_scale, np.float64)[None, :]
 
 
-def linear_rows(x, trellis, sign, out_scale, K, rows: np.ndarray) -> np.ndarray:
+def linear_rows(x, trellis, sign, out_scale, K, rows: np.ndarray, cb: int = 0) -> np.ndarray:
     """Selected output features only: y[:, rows] (decodes only the strips they lie in)."""
     m, n_in, n_out = _check_shapes(x, trellis, sign, out_scale, K)
     rows = np.asarray(rows, dtype=np.int64)
@@ -209,7 +244,7 @@ def linear_rows(x, trellis, sign, out_scale, K, rows: np.ndarray) -> np.ndarray:
     strips = np.unique(rows // 16)
     out = np.empty((m, rows.size), dtype=np.float64)
     for tr in strips:
-        W = dequant(trellis[tr:tr + 1], K).astype(np.float64)  # [16, n_in]
+        W = dequant(trellis[tr:tr + 1], K, cb).astype(np.float64)  # [16, n_in]
         sel = np.nonzero(rows // 16 == tr)[0]
         out[:, sel] = xr @ W[rows[sel] - 16 * tr].T
     return out * np.asarray(out_scale, np.float64)[rows][None, :]
@@ -263,8 +298,15 @@ def round_to_fp16(v: float) -> float:
     return math.copysign(out, v)
 
 
-def codebook_scalar(s: int) -> float:
-    """c(s) via Python integers (FMT-5)."""
+def codebook_scalar(s: int, cb: int = 0) -> float:
+    """c(s) via Python integers: FMT-5 (cb = 0) or FMT-10 (cb = 1)."""
+    if cb == 1:
+        from fractions import Fraction
+        p = (s * CB1_A + CB1_B) % (1 << 32)
+        t = sum((p >> (8 * k)) & 0xFF for k in range(4))
+        G = Fraction(_fp16_bits_to_float(CB1_G))
+        C = Fraction(_fp16_bits_to_float(CB1_C))
+        return round_to_fp16(float((1024 + t) * G + C))  # the rational is exact in a double
     p = (s * CB_A + CB_B) % (1 << 32)
     q = (p & CB_M) | CB_X
     lo = _fp16_bits_to_float(q & 0xFFFF)
@@ -276,7 +318,7 @@ def hadamard_entry(i: int, j: int) -> int:
     return -1 if bin(i & j).count("1") % 2 else 1
 
 
-def y_scalar(x, trellis, sign, out_scale, K: int, r: int, o: int) -> float:
+def y_scalar(x, trellis, sign, out_scale, K: int, r: int, o: int, cb: int = 0) -> float:
     """One output element straight from the definitions (FMT-1..7), pure Python.
 
     Quadratic in n_in: for tiny shapes only.
@@ -292,7 +334,7 @@ def y_scalar(x, trellis, sign, out_scale, K: int, r: int, o: int) -> float:
             xr += hadamard_entry(i, jj) * float(sign[col]) * float(x[r][col])
         tc, cc = divmod(k, 16)
         elem = rr * 16 + cc
-        w = codebook_scalar(state_scalar(trellis[tr][tc], K, elem))
+        w = codebook_scalar(state_scalar(trellis[tr][tc], K, elem), cb)
         acc += xr * w
     return float(out_scale[o]) * acc
 

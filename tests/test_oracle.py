@@ -122,6 +122,80 @@ def test_codebook_vectorised_equals_scalar_all_states():
     np.testing.assert_array_equal(c, cs)
 
 
+# ------------------------------------------------- byte-sum codebook (FMT-10) --
+def _golden_codebook1():
+    rows = []
+    with open(os.path.join(GOLDEN, "codebook1_examples.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            s, p, t, bits, val = line.split()
+            rows.append((int(s, 16), int(p, 16), int(t), int(bits, 16), float(val)))
+    return rows
+
+
+def test_codebook1_hand_worked_examples():
+    rows = _golden_codebook1()
+    assert len(rows) == 4
+    for s, p, t, bits, val in rows:
+        c = O.codebook(np.array([s], dtype=np.uint16), cb=1)
+        assert int(O.fp16_bits(c)[0]) == bits, hex(s)
+        assert float(c[0]) == val
+        assert O.codebook_scalar(s, cb=1) == val
+        assert int(O.byte_sums(np.array([s]))[0]) == t
+        assert (s * O.CB1_A + O.CB1_B) % (1 << 32) == p
+
+
+def test_codebook1_byte_sums_by_byte_view():
+    # the byte sum read back through a little-endian byte view of p: catches a
+    # wrong shift, mask or byte count in byte_sums
+    s = np.arange(65536, dtype=np.uint64)
+    p = ((s * np.uint64(O.CB1_A) + np.uint64(O.CB1_B)) & np.uint64(0xFFFFFFFF)).astype("<u4")
+    t = p.view(np.uint8).reshape(-1, 4).astype(np.int64).sum(axis=1)
+    np.testing.assert_array_equal(O.byte_sums(s), t)
+
+
+def test_codebook1_constants_and_statistics():
+    assert O.CB1_A % 2 == 1 and O.CB1_A < (1 << 16)
+    # G and C are fp16 values; C = -10.375 exactly, G = 1773/262144 exactly
+    G = float(np.array([O.CB1_G], np.uint16).view(np.float16)[0])
+    C = float(np.array([O.CB1_C], np.uint16).view(np.float16)[0])
+    assert G == 1773 / 262144 and C == -10.375
+    s = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    t = O.byte_sums(s).astype(np.float64)
+    # four uniform bytes: mean 4 * 255/2 = 510, variance 4 * (256^2 - 1)/12 = 21845
+    assert abs(t.mean() - 510) / 510 < 1e-3 and abs(t.var() - 21845) / 21845 < 2e-3
+    c = O.codebook(s, cb=1).astype(np.float64)
+    assert np.isfinite(c).all()
+    assert np.abs(c).min() >= 2.0 ** -14          # no subnormal value
+    assert abs(c.mean()) <= 0.01 and abs(c.var() - 1.0) <= 0.02
+    assert len(np.unique(c)) > 800
+
+
+def test_codebook1_single_rounding_all_states():
+    # exact rational (1024 + t) * G + C, rounded once to fp16 (Fraction path), on every state
+    s = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    c = O.codebook(s, cb=1).astype(np.float64)
+    cs = np.array([O.codebook_scalar(int(v), cb=1) for v in range(65536)])
+    np.testing.assert_array_equal(c, cs)
+
+
+def test_codebook1_is_affine_in_the_byte_sum():
+    # equal byte sums give equal values; values increase with the byte sum
+    s = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    t = O.byte_sums(s)
+    c = O.codebook(s, cb=1).astype(np.float64)
+    order = np.argsort(t, kind="stable")
+    assert np.all(np.diff(c[order]) >= 0)
+    for tv in np.unique(t)[::50]:
+        assert np.unique(c[t == tv]).size == 1
+
+
+def test_codebook_rejects_unknown_codebook():
+    with pytest.raises(ValueError):
+        O.codebook(np.array([0]), cb=2)
+
+
 # ------------------------------------------------------------------ states --
 @pytest.mark.parametrize("K", range(1, 9))
 def test_states_zero_and_ones_streams(K):
@@ -217,6 +291,20 @@ def test_linear_brute_force_tiny(K):
         o = int(rng.integers(0, n_out))
         ys = O.y_scalar(x, words, sign, scale, K, r, o)
         assert abs(y[r, o] - ys) <= 1e-9 * max(1.0, abs(ys))
+
+
+@pytest.mark.parametrize("K", [2, 5, 8])
+def test_linear_brute_force_tiny_codebook1(K):
+    words, x, sign, scale = synth.random_case(128, 16, K, 2, 250 + K)
+    y = O.linear(x, words, sign, scale, K, cb=1)
+    assert not np.allclose(y, O.linear(x, words, sign, scale, K))  # the codebook matters
+    rng = np.random.default_rng(K)
+    for _ in range(4):
+        r, o = int(rng.integers(0, 2)), int(rng.integers(0, 16))
+        ys = O.y_scalar(x, words, sign, scale, K, r, o, cb=1)
+        assert abs(y[r, o] - ys) <= 1e-9 * max(1.0, abs(ys))
+    rows = np.array([0, 7, 15])
+    np.testing.assert_allclose(O.linear_rows(x, words, sign, scale, K, rows, cb=1), y[:, rows], rtol=0, atol=1e-12)
 
 
 def test_linear_unit_input_closed_form():
