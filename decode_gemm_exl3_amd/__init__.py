@@ -11,6 +11,8 @@ Tensors:
   sign            : float16 [n_in] (+-1)
   out_scale       : float16 [n_out]
   result y        : float16 [m, n_out]
+Every call takes the bit width K and, as a keyword, the codebook (0: multiply,
+mask-and-plant, half sum; 1: byte sum), passed to the ABI as one bits argument.
 """
 from __future__ import annotations
 
@@ -18,11 +20,12 @@ import ctypes
 import os
 
 __all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemv_multi",
-           "gemm", "status_string", "MAX_PROJ"]
+           "gemm", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 MAX_PROJ = 4  # EXL3_GEMV_MAX_PROJ
+CODEBOOK_BYTE_SUM = 0x100  # EXL3_CODEBOOK_BYTE_SUM: flag in the bits argument selecting codebook 1
 
 
 class Exl3Error(RuntimeError):
@@ -72,6 +75,13 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+def bits_arg(bits: int, codebook: int = 0) -> int:
+    """The C ABI's bits argument: K, with the flag of codebook 1 when asked for."""
+    if codebook not in (0, 1):
+        raise Exl3Error(f"codebook must be 0 or 1, got {codebook}")
+    return int(bits) | (CODEBOOK_BYTE_SUM if codebook == 1 else 0)
+
+
 def status_string(status: int) -> str:
     return load().exl3_status_string(int(status)).decode()
 
@@ -114,17 +124,18 @@ class Workspace:
         return pack_info(n_in, n_out, bits, max(m, 1))["workspace_bytes"] <= self.nbytes
 
 
-def decode_tile(words, bits: int, out=None, stream=None):
+def decode_tile(words, bits: int, out=None, stream=None, codebook: int = 0):
     """Decode packed tiles [T, 16*bits] (int16) to fp16 [T, 256] in trellis order."""
     import torch
     T = words.shape[0]
     if out is None:
         out = torch.empty((T, 256), dtype=torch.float16, device=words.device)
-    _check(load().exl3_decode_tile(_ptr(words), bits, T, _ptr(out), _stream(stream)), "exl3_decode_tile")
+    _check(load().exl3_decode_tile(_ptr(words), bits_arg(bits, codebook), T, _ptr(out), _stream(stream)),
+           "exl3_decode_tile")
     return out
 
 
-def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
+def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook=0):
     import torch
     m, n_in = x.shape
     n_out = out_scale.shape[0]
@@ -132,18 +143,18 @@ def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=N
         y = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
     if workspace is None:
         workspace = Workspace(n_in, n_out, bits, max(m, 1), device=x.device)
-    rc = getattr(load(), fn)(_ptr(x), m, _ptr(trellis), _ptr(sign), _ptr(out_scale), n_in, n_out, bits,
-                             _ptr(y), _ptr(workspace.buf), workspace.nbytes, _stream(stream))
+    rc = getattr(load(), fn)(_ptr(x), m, _ptr(trellis), _ptr(sign), _ptr(out_scale), n_in, n_out,
+                             bits_arg(bits, codebook), _ptr(y), _ptr(workspace.buf), workspace.nbytes, _stream(stream))
     _check(rc, fn)
     return y
 
 
-def gemv(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
+def gemv(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):
     """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 8 (fp16 out)."""
-    return _linear("exl3_gemv", x, trellis, sign, out_scale, bits, workspace, y, stream)
+    return _linear("exl3_gemv", x, trellis, sign, out_scale, bits, workspace, y, stream, codebook)
 
 
-def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None):
+def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None, codebook: int = 0):
     """One launch for several projections of the same x (1 <= m <= 8).
 
     weights: sequence of (trellis, out_scale) pairs sharing n_in and bits; the
@@ -159,11 +170,12 @@ def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None
         arr[i] = _Proj(_ptr(tr), _ptr(sc), _ptr(y), int(sc.shape[0]), 0)
     ws = 0 if workspace is None else _ptr(workspace.buf)
     wsb = 0 if workspace is None else workspace.nbytes
-    rc = load().exl3_gemv_multi(_ptr(x), m, _ptr(sign), n_in, bits, arr, n, ws, wsb, _stream(stream))
+    rc = load().exl3_gemv_multi(_ptr(x), m, _ptr(sign), n_in, bits_arg(bits, codebook), arr, n, ws, wsb,
+                                _stream(stream))
     _check(rc, "exl3_gemv_multi")
     return ys
 
 
-def gemm(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None):
+def gemm(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):
     """The same result for any m >= 1 through the matrix-core GEMM path."""
-    return _linear("exl3_gemm", x, trellis, sign, out_scale, bits, workspace, y, stream)
+    return _linear("exl3_gemm", x, trellis, sign, out_scale, bits, workspace, y, stream, codebook)

@@ -91,8 +91,15 @@ bool plan_gemv(exl3::GemvParams* p) {
     return false;
 }
 
+// The bits argument: K in the low byte, the codebook flag above it.
+int k_of(int32_t bits) { return bits & 0xFF; }
+int cb_of(int32_t bits) { return (bits & EXL3_CODEBOOK_BYTE_SUM) ? 1 : 0; }
+bool bad_bits(int32_t bits) {
+    return k_of(bits) < 1 || k_of(bits) > 8 || (bits & ~(0xFF | EXL3_CODEBOOK_BYTE_SUM)) != 0;
+}
+
 bool bad_shape(int32_t n_in, int32_t n_out, int32_t bits) {
-    return n_in <= 0 || n_out <= 0 || (n_in % 128) != 0 || (n_out % 16) != 0 || bits < 1 || bits > 8;
+    return n_in <= 0 || n_out <= 0 || (n_in % 128) != 0 || (n_out % 16) != 0 || bad_bits(bits);
 }
 
 int common_checks(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
@@ -104,7 +111,7 @@ int common_checks(const uint16_t* x, int32_t m, const uint16_t* trellis, const u
     if ((const void*)x == (const void*)y) return EXL3_EINVAL;
     if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return EXL3_EWORKSPACE;
     // weights are read through 32-bit buffer offsets
-    if ((int64_t)n_in * n_out * bits / 8 >= ((int64_t)1 << 31) - ((int64_t)1 << 20)) return EXL3_EUNSUPPORTED;
+    if ((int64_t)n_in * n_out * k_of(bits) / 8 >= ((int64_t)1 << 31) - ((int64_t)1 << 20)) return EXL3_EUNSUPPORTED;
     return 1;  // proceed
 }
 
@@ -120,20 +127,20 @@ int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m, exl
     out->max_m = max_m;
     out->tiles_in = n_in / 16;
     out->tiles_out = n_out / 16;
-    out->words_per_tile = 16 * bits;
+    out->words_per_tile = 16 * k_of(bits);
     out->reserved = 0;
     out->trellis_words = (int64_t)out->tiles_in * out->tiles_out * out->words_per_tile;
-    out->trellis_bytes = (int64_t)n_in * n_out * bits / 8;
+    out->trellis_bytes = (int64_t)n_in * n_out * k_of(bits) / 8;
     out->workspace_bytes = ws_total(n_in, n_out, max_m);
     return EXL3_OK;
 }
 
 int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles, uint16_t* out, void* stream) {
-    if (bits < 1 || bits > 8 || n_tiles < 0) return EXL3_EINVAL;
+    if (bad_bits(bits) || n_tiles < 0) return EXL3_EINVAL;
     if (n_tiles == 0) return EXL3_OK;
     if (!words || !out) return EXL3_EINVAL;
     if (n_tiles > (int64_t)0xFFFFFFFF * 16) return EXL3_EUNSUPPORTED;
-    hipError_t e = exl3::launch_decode(bits, words, n_tiles, out, (hipStream_t)stream);
+    hipError_t e = exl3::launch_decode(k_of(bits), cb_of(bits), words, n_tiles, out, (hipStream_t)stream);
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
 }
 
@@ -142,7 +149,7 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
                     void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    if (m < 0 || m > 8 || bits < 1 || bits > 8 || n_in <= 0 || (n_in % 128) != 0) return EXL3_EINVAL;
+    if (m < 0 || m > 8 || bad_bits(bits) || n_in <= 0 || (n_in % 128) != 0) return EXL3_EINVAL;
     if (!proj || n_proj < 1 || n_proj > EXL3_GEMV_MAX_PROJ) return EXL3_EINVAL;
     for (int i = 0; i < n_proj; ++i) {
         const int32_t n_out = proj[i].n_out;
@@ -158,7 +165,7 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
         for (int j = 0; j < i; ++j)
             if (proj[j].y == q.y) return EXL3_EINVAL;
         // weights are read through 32-bit buffer offsets
-        if ((int64_t)n_in * q.n_out * bits / 8 >= ((int64_t)1 << 31) - ((int64_t)1 << 20)) return EXL3_EUNSUPPORTED;
+        if ((int64_t)n_in * q.n_out * k_of(bits) / 8 >= ((int64_t)1 << 31) - ((int64_t)1 << 20)) return EXL3_EUNSUPPORTED;
         strips += q.n_out / 16;
     }
     if (strips > ((int64_t)1 << 30)) return EXL3_EUNSUPPORTED;
@@ -181,7 +188,7 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
     p.tiles_in = n_in / 16;
     p.n_strips = (int)strips;
     if (!plan_gemv(&p)) return EXL3_EUNSUPPORTED;
-    hipError_t e = exl3::launch_gemv(bits, p, (hipStream_t)stream);
+    hipError_t e = exl3::launch_gemv(k_of(bits), cb_of(bits), p, (hipStream_t)stream);
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
 }
 
@@ -223,7 +230,7 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
     p.n_out = n_out;
     p.tiles_in = n_in / 16;
     p.n_strips = n_out / 16;
-    e = exl3::launch_gemm(bits, p, s);
+    e = exl3::launch_gemm(k_of(bits), cb_of(bits), p, s);
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
 }
 

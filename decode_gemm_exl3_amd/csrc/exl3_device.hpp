@@ -9,11 +9,16 @@
 // 0 for row 15) through a DPP row rotation inside its 16-lane row, so the
 // tile's wrap costs nothing.
 //
-// Codebook (table-free; pages: "GEMM kernel" - one integer multiply plus one
-// three-input bit operation per index; "conclusion first" - three instructions):
+// Codebooks (table-free; pages: "GEMM kernel" - an index becomes a half through
+// one integer multiply and either one three-input bit operation or one dp4a;
+// "conclusion first" - three instructions).  Both start with
 //   p = s*A + B (mod 2^32)      v_mad_u32_u16, state read from either 16-bit half
-//   q = (p & M) | X             v_and_or_b32
-//   value = lo(q) + hi(q)       fp16 add, or left to the matrix core (two k slots)
+// and produce a codebook word: a dword whose two fp16 halves sum to the value.
+//   codebook 0:  q = (p & M) | X                    v_and_or_b32
+//   codebook 1:  h = 0x6400 + (sum of p's bytes)    v_dot4_u32_u8 = fp16 bits of 1024 + t
+//                q = (h * G + C, 0 * G + 0)         v_pk_fma_f16, one rounding; high half +0
+// The GEMV leaves the halves' sum to the matrix core (two k slots per weight);
+// the GEMM and decode_tile form the fp16 value.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -25,6 +30,13 @@ constexpr uint32_t CB_A = 0xBFD3u;
 constexpr uint32_t CB_B = 0x201784FFu;
 constexpr uint32_t CB_M = 0x8D7F8DFFu;
 constexpr uint32_t CB_X = 0x30003000u;
+
+constexpr uint32_t CB1_A = 0xFEC5u;
+constexpr uint32_t CB1_B = 0x77C40AA0u;
+constexpr uint32_t CB1_ONES = 0x01010101u;  // dot4 weights: the byte sum
+constexpr uint32_t CB1_H = 0x6400u;         // fp16 1024: 0x6400 + t is the fp16 of 1024 + t (t <= 1020)
+constexpr uint32_t CB1_G2 = 0x1EED1EEDu;    // (G, G), G = 1773/262144
+constexpr uint32_t CB1_C2 = 0x0000C930u;    // (C, +0), C = -10.375
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -38,40 +50,63 @@ template <int K> struct RowGeom {
 };
 
 // Register-held codebook constants.  A VOP3 instruction on gfx9 reads at most
-// one SGPR or literal, so B and X live in VGPRs and A and M in SGPRs.  They are
-// produced by opaque moves so the compiler cannot fold them back into literals
-// (which would split the mask-and-plant into two instructions).
+// one SGPR or literal, so the additive constants live in VGPRs and the
+// multipliers and masks in SGPRs.  They are produced by opaque moves so the
+// compiler cannot fold them back into literals (which would split the
+// mask-and-plant into two instructions).
 struct CbRegs {
-    uint32_t vB, vX, sM;
+    uint32_t vB, vX, sM;  // codebook 0: B, X, M; codebook 1: B', 0x6400, 0x01010101
+    uint32_t vG2, vC2;    // codebook 1: (G, G) and (C, +0)
 };
 
+template <int CB>
 __device__ __forceinline__ CbRegs cb_regs() {
     CbRegs r;
-    uint32_t b = CB_B, x = CB_X, m = CB_M;
+    uint32_t b = CB == 0 ? CB_B : CB1_B, x = CB == 0 ? CB_X : CB1_H, m = CB == 0 ? CB_M : CB1_ONES;
     asm volatile("v_mov_b32 %0, %1" : "=v"(r.vB) : "s"(b));
     asm volatile("v_mov_b32 %0, %1" : "=v"(r.vX) : "s"(x));
     asm volatile("s_mov_b32 %0, %1" : "=s"(r.sM) : "s"(m));
+    r.vG2 = CB1_G2;
+    r.vC2 = CB1_C2;
+    if (CB == 1) {
+        uint32_t g = CB1_G2, c = CB1_C2;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(r.vG2) : "s"(g));
+        asm volatile("v_mov_b32 %0, %1" : "=v"(r.vC2) : "s"(c));
+    }
     return r;
+}
+
+// Word from p.  In C so that the compiler sees the VALU write that feeds the
+// matrix core and inserts the wait states an MFMA source read requires.
+template <int CB>
+__device__ __forceinline__ uint32_t cb_word(uint32_t p, const CbRegs& r) {
+    if constexpr (CB == 0) {
+        return (p & r.sM) | r.vX;
+    } else {
+        typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+        const uint32_t h = __builtin_amdgcn_udot4(p, r.sM, r.vX, false);
+        const h2_t v = __builtin_elementwise_fma(__builtin_bit_cast(h2_t, h), __builtin_bit_cast(h2_t, r.vG2),
+                                                 __builtin_bit_cast(h2_t, r.vC2));
+        return __builtin_bit_cast(uint32_t, v);
+    }
 }
 
 // The multiply reads the state from either 16-bit half of a register
 // (v_mad_u32_u16 with op_sel), which has no C spelling, so it is inline asm.
-// The mask-and-plant stays in C: it feeds the matrix core, and the compiler must
-// see that VALU write to insert the wait states an MFMA source read requires.
-__device__ __forceinline__ uint32_t cb_mask(uint32_t p, const CbRegs& r) { return (p & r.sM) | r.vX; }
-
 // Codebook word for the state held in the low 16 bits of w.
+template <int CB>
 __device__ __forceinline__ uint32_t cb_lo(uint32_t w, const CbRegs& r) {
     uint32_t p;
-    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(p) : "v"(w), "s"(CB_A), "v"(r.vB));
-    return cb_mask(p, r);
+    asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(p) : "v"(w), "s"(CB == 0 ? CB_A : CB1_A), "v"(r.vB));
+    return cb_word<CB>(p, r);
 }
 
 // Codebook word for the state held in the high 16 bits of w.
+template <int CB>
 __device__ __forceinline__ uint32_t cb_hi(uint32_t w, const CbRegs& r) {
     uint32_t p;
-    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(p) : "v"(w), "s"(CB_A), "v"(r.vB));
-    return cb_mask(p, r);
+    asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(p) : "v"(w), "s"(CB == 0 ? CB_A : CB1_A), "v"(r.vB));
+    return cb_word<CB>(p, r);
 }
 
 // fp16 sum of the two halves of a codebook word, round to nearest even.
@@ -79,6 +114,20 @@ __device__ __forceinline__ uint16_t cb_sum(uint32_t q) {
     __half lo = __ushort_as_half((unsigned short)(q & 0xFFFFu));
     __half hi = __ushort_as_half((unsigned short)(q >> 16));
     return __half_as_ushort(__hadd(lo, hi));
+}
+
+// The fp16 value of a codebook word (bit pattern).
+template <int CB>
+__device__ __forceinline__ uint16_t cb_value(uint32_t q) {
+    if constexpr (CB == 0) return cb_sum(q);
+    else return (uint16_t)q;  // the high half is +0
+}
+
+// Two values packed as one fp16x2 dword (first in the low half).
+template <int CB>
+__device__ __forceinline__ uint32_t cb_pack(uint32_t q0, uint32_t q1) {
+    if constexpr (CB == 0) return (uint32_t)cb_sum(q0) | ((uint32_t)cb_sum(q1) << 16);
+    else return (q0 & 0xFFFFu) | (q1 << 16);
 }
 
 // Dword of the lane that owns the next row of the same tile (row 15 -> row 0):
@@ -140,7 +189,7 @@ __device__ __forceinline__ void finish_row(int n, uint32_t (&b)[RowGeom<K>::NB])
 // Codebook words of the 16 states of a finished row: q[c] for state c.
 // All offsets are compile-time constants; windows at bit 0 or 16 of a dword are
 // read in place, and when K divides 16 one funnel shift serves two states.
-template <int K>
+template <int K, int CB>
 __device__ __forceinline__ void decode_row(const uint32_t (&b)[RowGeom<K>::NB], uint32_t (&q)[16],
                                            const CbRegs& r) {
     constexpr int NB = RowGeom<K>::NB;
@@ -151,17 +200,17 @@ __device__ __forceinline__ void decode_row(const uint32_t (&b)[RowGeom<K>::NB], 
         const int dw = P >> 5;
         const int sh = P & 31;
         if (sh == 0) {
-            q[c] = cb_lo(b[dw], r);
+            q[c] = cb_lo<CB>(b[dw], r);
         } else if (sh == 16) {
-            q[c] = cb_hi(b[dw], r);
+            q[c] = cb_hi<CB>(b[dw], r);
         } else if (pairs && sh > 16) {
             // produced together with state c - 16/K (same funnel shift, high half)
         } else {
             // a window that ends inside b[dw] may take any high operand
             const uint32_t w = __builtin_amdgcn_alignbit(b[(dw + 1 < NB) ? dw + 1 : dw], b[dw],
                                                          (uint32_t)sh);
-            q[c] = cb_lo(w, r);
-            if (pairs && c + 16 / K < 16) q[(c + 16 / K) & 15] = cb_hi(w, r);
+            q[c] = cb_lo<CB>(w, r);
+            if (pairs && c + 16 / K < 16) q[(c + 16 / K) & 15] = cb_hi<CB>(w, r);
         }
     }
 }
@@ -192,7 +241,7 @@ __device__ __forceinline__ uint32_t half_shift(int n, int h) {
 }
 
 // Codebook words of the 8 states of a normalised half row (state c at bit cK).
-template <int K>
+template <int K, int CB>
 __device__ __forceinline__ void decode_half(const uint32_t (&b)[HalfGeom<K>::KDH], uint32_t (&q)[8],
                                             const CbRegs& r) {
     constexpr int NB = HalfGeom<K>::KDH;
@@ -203,15 +252,15 @@ __device__ __forceinline__ void decode_half(const uint32_t (&b)[HalfGeom<K>::KDH
         const int dw = P >> 5;
         const int sh = P & 31;
         if (sh == 0) {
-            q[c] = cb_lo(b[dw], r);
+            q[c] = cb_lo<CB>(b[dw], r);
         } else if (sh == 16) {
-            q[c] = cb_hi(b[dw], r);
+            q[c] = cb_hi<CB>(b[dw], r);
         } else if (pairs && sh > 16 && c - 16 / K >= 0) {
             // produced together with state c - 16/K
         } else {
             const uint32_t w = __builtin_amdgcn_alignbit(b[(dw + 1 < NB) ? dw + 1 : dw], b[dw], (uint32_t)sh);
-            q[c] = cb_lo(w, r);
-            if (pairs && c + 16 / K < 8) q[(c + 16 / K) & 7] = cb_hi(w, r);
+            q[c] = cb_lo<CB>(w, r);
+            if (pairs && c + 16 / K < 8) q[(c + 16 / K) & 7] = cb_hi<CB>(w, r);
         }
     }
 }

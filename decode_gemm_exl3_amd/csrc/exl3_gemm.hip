@@ -33,7 +33,7 @@ constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 by
 constexpr int GM_A_HALVES = GM_BM * GM_LD;
 constexpr int GM_B_FRAGS = 2 * 4 * 4 * 64;  // [k half][output quarter][fragment][lane], 16 bytes each
 
-template <int K>
+template <int K, int CB>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     __shared__ __align__(16) uint16_t As[2][GM_A_HALVES];
     __shared__ __align__(16) u32x4_t Bs[2][GM_B_FRAGS];
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
     const int m0 = (lin / nbx) * GM_BM;
     const int s0 = (lin % nbx) * (GM_BN / 16) + 4 * nq;  // first strip of this wave
-    const CbRegs cr = cb_regs();
+    const CbRegs cr = cb_regs<CB>();
 
     // ---- weights: fragment j = strip s0 + j, tile column 2 mh + (g >> 1) of the
     // step, half g & 1 of row n.  Lane offsets are fixed; strip and step go in
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
                     d[i] = __builtin_amdgcn_alignbit(rows[j][i + 1 < KDH ? i + 1 : i], rows[j][i], bsh);
             }
             uint32_t q[8];
-            decode_half<K>(d, q, cr);
+            decode_half<K, CB>(d, q, cr);
             // refill after the decode has consumed the rows, into the same
             // registers (the fences keep the scheduler from hoisting the loads,
             // which would force copies and a wait for them)
@@ -94,8 +94,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
             uint32_t o[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                o[e] = (uint32_t)cb_sum(q[2 * e]) | ((uint32_t)cb_sum(q[2 * e + 1]) << 16);
+            for (int e = 0; e < 4; ++e) o[e] = cb_pack<CB>(q[2 * e], q[2 * e + 1]);
             Bs[buf][((mh * 4 + nq) * 4 + j) * 64 + lane] = u32x4_t{o[0], o[1], o[2], o[3]};
         }
     };
@@ -197,25 +196,30 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-template <int K>
+template <int K, int CB>
 static hipError_t launch_gemm_k(const GemmParams& p, hipStream_t s) {
     dim3 grid((p.n_strips + 15) / 16, (p.m + GM_BM - 1) / GM_BM);
-    hipLaunchKernelGGL(gemm_kernel<K>, grid, dim3(512), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<K, CB>), grid, dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(int K, const GemmParams& p, hipStream_t s) {
+template <int CB>
+static hipError_t launch_gemm_cb(int K, const GemmParams& p, hipStream_t s) {
     switch (K) {
-        case 1: return launch_gemm_k<1>(p, s);
-        case 2: return launch_gemm_k<2>(p, s);
-        case 3: return launch_gemm_k<3>(p, s);
-        case 4: return launch_gemm_k<4>(p, s);
-        case 5: return launch_gemm_k<5>(p, s);
-        case 6: return launch_gemm_k<6>(p, s);
-        case 7: return launch_gemm_k<7>(p, s);
-        case 8: return launch_gemm_k<8>(p, s);
+        case 1: return launch_gemm_k<1, CB>(p, s);
+        case 2: return launch_gemm_k<2, CB>(p, s);
+        case 3: return launch_gemm_k<3, CB>(p, s);
+        case 4: return launch_gemm_k<4, CB>(p, s);
+        case 5: return launch_gemm_k<5, CB>(p, s);
+        case 6: return launch_gemm_k<6, CB>(p, s);
+        case 7: return launch_gemm_k<7, CB>(p, s);
+        case 8: return launch_gemm_k<8, CB>(p, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(int K, int cb, const GemmParams& p, hipStream_t s) {
+    return cb == 0 ? launch_gemm_cb<0>(K, p, s) : launch_gemm_cb<1>(K, p, s);
 }
 
 }  // namespace exl3

@@ -46,10 +46,11 @@ struct GemmParams {
     int tiles_in, n_strips;
 };
 
-hipError_t launch_decode(int K, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s);
+// cb selects the codebook: 0 (multiply, mask-and-plant, half sum) or 1 (byte sum)
+hipError_t launch_decode(int K, int cb, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s);
 hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr,
                          hipStream_t s);
-hipError_t launch_gemv(int K, const GemvParams& p, hipStream_t s);
-hipError_t launch_gemm(int K, const GemmParams& p, hipStream_t s);
+hipError_t launch_gemv(int K, int cb, const GemvParams& p, hipStream_t s);
+hipError_t launch_gemm(int K, int cb, const GemmParams& p, hipStream_t s);
 
 }  // namespace exl3

@@ -8,10 +8,10 @@ namespace exl3 {
 
 // ---------------------------------------------------------------------------
 // decode_tile: one wave decodes 4 tiles, lane (n, g) = row n of tile 4*wave + g.
-// Output is the fp16 sum of the halves (bit-exact codebook value), in trellis
-// order: element 16n + c of the tile.
+// Output is the bit-exact fp16 codebook value, in trellis order: element 16n + c
+// of the tile.
 // ---------------------------------------------------------------------------
-template <int K>
+template <int K, int CB>
 __global__ __launch_bounds__(256) void decode_tile_kernel(const uint16_t* __restrict__ words,
                                                           int64_t n_tiles, uint16_t* __restrict__ out) {
     const int lane = threadIdx.x & 63;
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(const uint16_t* __rest
     const int64_t tile0 = (int64_t)blockIdx.x * 16;
     const int64_t tile = tile0 + (threadIdx.x >> 6) * 4 + (lane >> 4);
     const bool valid = tile < n_tiles;
-    const CbRegs cr = cb_regs();
+    const CbRegs cr = cb_regs<CB>();
     // tiles past the end read as zero through the buffer range check
     const __amdgpu_buffer_rsrc_t rs =
         make_rsrc(reinterpret_cast<const char*>(words) + tile0 * TILE_B, (n_tiles - tile0) * TILE_B);
@@ -28,11 +28,11 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(const uint16_t* __rest
     load_row<K>(rs, (uint32_t)((tile - tile0) * TILE_B) + row_offset<K>(n), 0u, b);
     finish_row<K>(n, b);  // every lane takes part in the DPP
     uint32_t q[16];
-    decode_row<K>(b, q, cr);
+    decode_row<K, CB>(b, q, cr);
     if (valid) {
         uint32_t o[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = (uint32_t)cb_sum(q[2 * j]) | ((uint32_t)cb_sum(q[2 * j + 1]) << 16);
+        for (int j = 0; j < 8; ++j) o[j] = cb_pack<CB>(q[2 * j], q[2 * j + 1]);
         u32x4_t* dst = reinterpret_cast<u32x4_t*>(out + tile * 256 + n * 16);
         dst[0] = u32x4_t{o[0], o[1], o[2], o[3]};
         dst[1] = u32x4_t{o[4], o[5], o[6], o[7]};
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict_
 // barrier); at the end the waves' sums are added and y is written.  One kernel,
 // no cross-workgroup reduction.
 // ---------------------------------------------------------------------------
-template <int K, int PF>
+template <int K, int PF, int CB>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     // LDS: x' rows [m][xcols] | zero block [PF * 64] | partial sums [nj][W][m][16]
     extern __shared__ __align__(16) uint32_t xs[];
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     for (int i = tid; i < nj * W * M * 16; i += 64 * W) red[i] = 0.f;
 
     const bool adata = n < M;
-    const CbRegs cr = cb_regs();
+    const CbRegs cr = cb_regs<CB>();
     int q = 0;
     for (int c = 0; c < p.n_kchunks; ++c) {
         const int tc0 = c * p.kc;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                     // so the wait before each step covers only its own load
                     finish_row<K>(n, buf[u]);
                     uint32_t qq[16];
-                    decode_row<K>(buf[u], qq, cr);
+                    decode_row<K, CB>(buf[u], qq, cr);
                     __builtin_amdgcn_sched_barrier(0);
                     load_row<K>(rref, loff, min(roff + u * STEP_B, rlim), buf[u]);
                     // the refill stays here: the scheduler would otherwise sink the
@@ -321,25 +321,30 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
 // ---------------------------------------------------------------------------
 // host-side launchers
 // ---------------------------------------------------------------------------
-template <int K>
+template <int K, int CB>
 static hipError_t launch_decode_k(const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s) {
     const int64_t blocks = (n_tiles + 15) / 16;
-    hipLaunchKernelGGL(decode_tile_kernel<K>, dim3((unsigned)blocks), dim3(256), 0, s, words, n_tiles, out);
+    hipLaunchKernelGGL((decode_tile_kernel<K, CB>), dim3((unsigned)blocks), dim3(256), 0, s, words, n_tiles, out);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int K, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s) {
+template <int CB>
+static hipError_t launch_decode_cb(int K, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s) {
     switch (K) {
-        case 1: return launch_decode_k<1>(words, n_tiles, out, s);
-        case 2: return launch_decode_k<2>(words, n_tiles, out, s);
-        case 3: return launch_decode_k<3>(words, n_tiles, out, s);
-        case 4: return launch_decode_k<4>(words, n_tiles, out, s);
-        case 5: return launch_decode_k<5>(words, n_tiles, out, s);
-        case 6: return launch_decode_k<6>(words, n_tiles, out, s);
-        case 7: return launch_decode_k<7>(words, n_tiles, out, s);
-        case 8: return launch_decode_k<8>(words, n_tiles, out, s);
+        case 1: return launch_decode_k<1, CB>(words, n_tiles, out, s);
+        case 2: return launch_decode_k<2, CB>(words, n_tiles, out, s);
+        case 3: return launch_decode_k<3, CB>(words, n_tiles, out, s);
+        case 4: return launch_decode_k<4, CB>(words, n_tiles, out, s);
+        case 5: return launch_decode_k<5, CB>(words, n_tiles, out, s);
+        case 6: return launch_decode_k<6, CB>(words, n_tiles, out, s);
+        case 7: return launch_decode_k<7, CB>(words, n_tiles, out, s);
+        case 8: return launch_decode_k<8, CB>(words, n_tiles, out, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(int K, int cb, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s) {
+    return cb == 0 ? launch_decode_cb<0>(K, words, n_tiles, out, s) : launch_decode_cb<1>(K, words, n_tiles, out, s);
 }
 
 hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr, hipStream_t s) {
@@ -348,7 +353,7 @@ hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_i
     return hipGetLastError();
 }
 
-template <int K, int PF>
+template <int K, int PF, int CB>
 static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
     const size_t lds = gemv_lds_bytes(p.m, p.waves, p.nsw, PF, (p.n_strips + p.grid - 1) / p.grid);
     // allow more than 64 KB of dynamic LDS, once per device
@@ -357,37 +362,42 @@ static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     const unsigned long long bit = 1ull << (dev & 63);
     if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF, CB>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_BUDGET);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((gemv_kernel<K, PF>), dim3(p.grid), dim3(64 * p.waves), lds, s, p);
+    hipLaunchKernelGGL((gemv_kernel<K, PF, CB>), dim3(p.grid), dim3(64 * p.waves), lds, s, p);
     return hipGetLastError();
 }
 
-template <int K>
+template <int K, int CB>
 static hipError_t launch_gemv_k(const GemvParams& p, hipStream_t s) {
     switch (p.pf) {
-        case 2: return launch_gemv_kp<K, 2>(p, s);
-        case 4: return launch_gemv_kp<K, 4>(p, s);
-        case 8: return launch_gemv_kp<K, 8>(p, s);
+        case 2: return launch_gemv_kp<K, 2, CB>(p, s);
+        case 4: return launch_gemv_kp<K, 4, CB>(p, s);
+        case 8: return launch_gemv_kp<K, 8, CB>(p, s);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemv(int K, const GemvParams& p, hipStream_t s) {
+template <int CB>
+static hipError_t launch_gemv_cb(int K, const GemvParams& p, hipStream_t s) {
     switch (K) {
-        case 1: return launch_gemv_k<1>(p, s);
-        case 2: return launch_gemv_k<2>(p, s);
-        case 3: return launch_gemv_k<3>(p, s);
-        case 4: return launch_gemv_k<4>(p, s);
-        case 5: return launch_gemv_k<5>(p, s);
-        case 6: return launch_gemv_k<6>(p, s);
-        case 7: return launch_gemv_k<7>(p, s);
-        case 8: return launch_gemv_k<8>(p, s);
+        case 1: return launch_gemv_k<1, CB>(p, s);
+        case 2: return launch_gemv_k<2, CB>(p, s);
+        case 3: return launch_gemv_k<3, CB>(p, s);
+        case 4: return launch_gemv_k<4, CB>(p, s);
+        case 5: return launch_gemv_k<5, CB>(p, s);
+        case 6: return launch_gemv_k<6, CB>(p, s);
+        case 7: return launch_gemv_k<7, CB>(p, s);
+        case 8: return launch_gemv_k<8, CB>(p, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemv(int K, int cb, const GemvParams& p, hipStream_t s) {
+    return cb == 0 ? launch_gemv_cb<0>(K, p, s) : launch_gemv_cb<1>(K, p, s);
 }
 
 }  // namespace exl3

@@ -18,8 +18,14 @@
  *     strip (fixed tr) is contiguous.  Tile element i is W[16tr + i/16][16tc + i%16].
  *   - Stream bit j of a tile is bit (j % 16) of word j / 16.  State
  *     s_i = bits [iK, iK+16) of the stream, taken cyclically (i = 0..255).
- *   - Codebook: p = s*0xBFD3 + 0x201784FF (mod 2^32); q = (p & 0x8D7F8DFF) | 0x30003000;
+ *   - Codebook 0 (the multiply and three-input bit operation of "GEMM kernel"):
+ *     p = s*0xBFD3 + 0x201784FF (mod 2^32); q = (p & 0x8D7F8DFF) | 0x30003000;
  *     the value is the fp16 sum, rounded to nearest even, of q's two fp16 halves.
+ *   - Codebook 1 (the dp4a alternative the same section names): p = s*0xFEC5 +
+ *     0x77C40AA0 (mod 2^32); t = the sum of p's four bytes; the value is
+ *     (1024 + t) * G + C rounded once to fp16 (nearest even), G = fp16 0x1EED
+ *     (1773/262144), C = fp16 0xC930 (-10.375).
+ *     A call selects it with EXL3_CODEBOOK_BYTE_SUM in its `bits` argument.
  *   - H128 is the unnormalised 128x128 Sylvester matrix, H[i][j] = (-1)^popcount(i&j),
  *     applied to each block of 128 consecutive input features.
  *   - fp16 values travel as uint16_t bit patterns.
@@ -46,6 +52,11 @@
 extern "C" {
 #endif
 
+/* The `bits` argument of every call: K (1..8) in the low byte, optionally OR-ed
+ * with EXL3_CODEBOOK_BYTE_SUM to select codebook 1.  Any other bit is EXL3_EINVAL.
+ * Sizes (trellis, workspace) depend on K only. */
+#define EXL3_CODEBOOK_BYTE_SUM 0x100
+
 enum exl3_status {
     EXL3_OK = 0,
     EXL3_EINVAL = -1,       /* null pointer, bad shape, bad bit width, bad m        */
@@ -55,18 +66,18 @@ enum exl3_status {
 };
 
 typedef struct exl3_pack_info_t {
-    int32_t n_in, n_out, bits, max_m; /* echo of the arguments                        */
+    int32_t n_in, n_out, bits, max_m; /* echo of the arguments (bits with its flag)    */
     int32_t tiles_in, tiles_out;      /* n_in / 16, n_out / 16                         */
-    int32_t words_per_tile;           /* 16 * bits                                     */
+    int32_t words_per_tile;           /* 16 * K                                        */
     int32_t reserved;
     int64_t trellis_words;            /* tiles_in * tiles_out * words_per_tile         */
-    int64_t trellis_bytes;            /* n_in * n_out * bits / 8                       */
+    int64_t trellis_bytes;            /* n_in * n_out * K / 8                          */
     int64_t workspace_bytes;          /* enough for exl3_gemv and exl3_gemm, any m <= max_m */
 } exl3_pack_info_t;
 
 /*
  * exl3_pack_info: sizes of the packed weight and of the workspace.
- *   n_in % 128 == 0, n_out % 16 == 0, 1 <= bits <= 8, max_m >= 1.
+ *   n_in % 128 == 0, n_out % 16 == 0, 1 <= K <= 8, max_m >= 1.
  * Host-only; never touches the GPU.  Returns EXL3_EINVAL on bad arguments.
  */
 int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m,
@@ -76,11 +87,11 @@ int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m,
  * exl3_decode_tile: decode n_tiles packed tiles (pages: "Viterbi encoding
  * kernel" packs each 16x16 block as a 16-bit index sequence; "GEMM kernel"
  * turns an index into a half with a multiply and a bit operation).
- *   words : uint16 [n_tiles][16*bits], device.
+ *   words : uint16 [n_tiles][16*K], device.
  *   out   : fp16 bits [n_tiles][256], device; element i of tile t at out[256t + i]
  *           (trellis order = row-major over the 16x16 tile).  Bit-exact.
  * n_tiles == 0 is a no-op.  EXL3_EINVAL for null pointers, n_tiles < 0 or a bad
- * bit width.
+ * bits argument.
  */
 int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
                      uint16_t* out, void* stream);
@@ -89,7 +100,7 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
  * exl3_gemv: the decode-matmul for 1 <= m <= 8 (pages: "small-batch GEMV",
  * where small m makes the weight stream the bottleneck).
  *   x         : fp16 [m][n_in]
- *   trellis   : uint16 [n_out/16][n_in/16][16*bits]
+ *   trellis   : uint16 [n_out/16][n_in/16][16*K]
  *   sign      : fp16 [n_in], entries +-1
  *   out_scale : fp16 [n_out]
  *   y         : fp16 [m][n_out] (overwritten; fp32 accumulation, round to nearest even)
@@ -108,7 +119,7 @@ int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
 
 /* One projection of an exl3_gemv_multi call (host memory; read during the call only). */
 typedef struct exl3_proj_t {
-    const uint16_t* trellis;   /* uint16 [n_out/16][n_in/16][16*bits], device   */
+    const uint16_t* trellis;   /* uint16 [n_out/16][n_in/16][16*K], device      */
     const uint16_t* out_scale; /* fp16 [n_out], device                          */
     uint16_t* y;               /* fp16 [m][n_out], device, overwritten          */
     int32_t n_out;             /* n_out % 16 == 0                               */

@@ -53,6 +53,22 @@ def test_pack_info_rejects(lib, args):
     assert lib.exl3_pack_info(128, 16, 4, 1, None) == -1
 
 
+def test_codebook_flag_in_bits(lib):
+    info = ex._PackInfo()
+    flag = ex.CODEBOOK_BYTE_SUM
+    assert flag == 0x100
+    assert lib.exl3_pack_info(4096, 4096, 4 | flag, 1, ctypes.byref(info)) == 0
+    assert info.bits == 4 | flag and info.words_per_tile == 64 and info.trellis_bytes == 4096 * 4096 // 2
+    for bad in (0 | flag, 9 | flag, 4 | 0x200, 4 | 0x10000, -4):
+        assert lib.exl3_pack_info(4096, 4096, bad, 1, ctypes.byref(info)) == -1, hex(bad)
+        assert lib.exl3_decode_tile(1, bad, 1, 2, None) == -1
+        assert _gemv_call(lib, "exl3_gemv", bits=bad) == -1
+        assert _gemv_call(lib, "exl3_gemm", bits=bad) == -1
+    assert ex.bits_arg(3, 1) == 3 | flag and ex.bits_arg(3) == 3
+    with pytest.raises(ex.Exl3Error):
+        ex.bits_arg(3, 2)
+
+
 def test_status_strings(lib):
     for code in (0, -1, -2, -3, -4, 7):
         s = ex.status_string(code)

@@ -41,19 +41,19 @@ def rel_fro(y, ref):
     return float(np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300))
 
 
-def run_linear(torch, fn, words, x, sign, scale, K, ws=None):
+def run_linear(torch, fn, words, x, sign, scale, K, ws=None, cb=0):
     import decode_gemm_exl3_amd as ex
     y = getattr(ex, fn)(to_dev(torch, x), to_dev(torch, words), to_dev(torch, sign), to_dev(torch, scale), K,
-                        workspace=ws)
+                        workspace=ws, codebook=cb)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 
 
 # --------------------------------------------------------------- decode -----
-def decode_gpu(torch, words, K):
+def decode_gpu(torch, words, K, cb=0):
     import decode_gemm_exl3_amd as ex
     w = to_dev(torch, words.reshape(-1, 16 * K))
-    out = ex.decode_tile(w, K)
+    out = ex.decode_tile(w, K, codebook=cb)
     torch.cuda.synchronize()
     return out.cpu().numpy().view(np.uint16)
 
@@ -110,6 +110,76 @@ def test_decode_deterministic(torch_cuda):
     a = decode_gpu(torch_cuda, words, 3)
     b = decode_gpu(torch_cuda, words, 3)
     assert np.array_equal(a, b)
+
+
+# --------------------------------------------------- byte-sum codebook -----
+@pytest.mark.parametrize("K", range(1, 9))
+def test_decode_codebook1_bit_exact(torch_cuda, K):
+    log(f"decode codebook 1 K={K}")
+    rng = np.random.default_rng(1100 + K)
+    for T in (1, 5, 1000):
+        words = rng.integers(0, 65536, (T, 16 * K), dtype=np.uint16)
+        got = decode_gpu(torch_cuda, words, K, cb=1)
+        ref = O.fp16_bits(O.decode_tiles(words, K, cb=1))
+        assert np.array_equal(got, ref), (K, T, np.argwhere(got != ref)[:5])
+    zero = decode_gpu(torch_cuda, np.zeros((1, 16 * K), np.uint16), K, cb=1)
+    assert (zero == 0xB168).all()  # c'(0), worked by hand in tests/golden/codebook1_examples.txt
+
+
+def test_decode_codebook1_all_states_k8(torch_cuda):
+    log("decode codebook 1 all states K=8")
+    tiles = []
+    for a in range(256):
+        for half in range(2):
+            bts = np.zeros(256, np.uint8)
+            bts[0::2] = a
+            bts[1::2] = np.arange(128) + 128 * half
+            tiles.append(bts.view(np.uint16))
+    words = np.stack(tiles)
+    got = decode_gpu(torch_cuda, words, 8, cb=1)
+    assert np.array_equal(got, O.fp16_bits(O.decode_tiles(words, 8, cb=1)))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("fn", ["gemv", "gemm"])
+def test_linear_codebook1_small_shapes(torch_cuda, fn, K):
+    for (n_in, n_out) in [(128, 16), (384, 272), (1024, 1040)]:
+        for m in ((1, 3, 8) if fn == "gemv" else (1, 33, 300)):
+            log(f"{fn} codebook 1 K={K} n_in={n_in} n_out={n_out} m={m}")
+            words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [17, K, n_in, n_out, m])
+            ref = O.linear(x, words, sign, scale, K, cb=1)
+            y = run_linear(torch_cuda, fn, words, x, sign, scale, K, cb=1)
+            assert np.isfinite(y).all()
+            err = rel_fro(y, ref)
+            assert err <= TOL, (fn, K, n_in, n_out, m, err)
+            if n_in == 1024:  # the codebook is in use: codebook 0 gives another result
+                assert rel_fro(y, O.linear(x, words, sign, scale, K)) > 0.5
+
+
+def test_codebook1_workloads(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    rng = np.random.default_rng(4)
+    cases = [("gemv", synth.Matmul("gate_k4_cb1", 4096, 14336, 4, 1, [0, 6, 0])),
+             ("gemv", synth.Matmul("down_k3_cb1_m8", 14336, 4096, 3, 8, [0, 6, 1])),
+             ("gemm", synth.Matmul("attn_8192_k4_cb1", 8192, 8192, 4, 2048, [0, 6, 2]))]
+    ws = ex.Workspace(14336, 14336, 8, 2048)
+    for fn, mm in cases:
+        log(f"{fn} codebook 1 {mm.name}")
+        words, x, sign, scale = synth.draw(mm)
+        y = run_linear(torch_cuda, fn, words, x, sign, scale, mm.K, ws=ws, cb=1)
+        rows = sampled_rows(mm.n_out, rng)
+        err = rel_fro(y[:, rows], O.linear_rows(x, words, sign, scale, mm.K, rows, cb=1))
+        assert err <= TOL, (mm.name, err)
+
+
+def test_gemv_multi_codebook1(torch_cuda):
+    import decode_gemm_exl3_amd as ex
+    words, x, sign, scales = group_case(1024, (272, 48, 16), 5, 2, 500)
+    ys = ex.gemv_multi(to_dev(torch_cuda, x), [(to_dev(torch_cuda, w), to_dev(torch_cuda, sc)) for w, sc in zip(words, scales)],
+                       to_dev(torch_cuda, sign), 5, codebook=1)
+    torch_cuda.cuda.synchronize()
+    for w, sc, y in zip(words, scales, ys):
+        assert rel_fro(y.cpu().numpy(), O.linear(x, w, sign, sc, 5, cb=1)) <= TOL
 
 
 # ----------------------------------------------------------------- gemv -----
