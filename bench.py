@@ -85,11 +85,12 @@ def build_mlp(torch, ex, m, Ks=(2, 3, 4), replicas=7, seed_base=0):
 
 
 def launch(ex, c, rep):
+    cb = c.get("codebook", 0)
     if len(c["n_outs"]) == 1:
-        ex.gemv(c["x"], c["words"][0][rep], c["sign"], c["scales"][0], c["K"], y=c["ys"][0])
+        ex.gemv(c["x"], c["words"][0][rep], c["sign"], c["scales"][0], c["K"], y=c["ys"][0], codebook=cb)
     else:
         ex.gemv_multi(c["x"], [(w[rep], sc) for w, sc in zip(c["words"], c["scales"])], c["sign"], c["K"],
-                      ys=c["ys"])
+                      ys=c["ys"], codebook=cb)
 
 
 def run_step(ex, calls, rep):
@@ -165,7 +166,7 @@ def copy_bandwidth(torch, nbytes=1 << 30, iters=10):
     return 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def gemm_tflops(torch, ex, iters=5):
+def gemm_tflops(torch, ex, iters=5, codebook=0):
     """Prefill GEMM: m=2048, 8192->8192 at K=4 (context figure for the second metric)."""
     import synth
     m, n_in, n_out, K = 2048, 8192, 8192, 4
@@ -175,13 +176,13 @@ def gemm_tflops(torch, ex, iters=5):
     scale = torch.full((n_out,), 0.02, dtype=torch.float16, device="cuda")
     y = torch.empty((m, n_out), dtype=torch.float16, device="cuda")
     ws = ex.Workspace(n_in, n_out, K, m)
-    ex.gemm(x, w, sign, scale, K, workspace=ws, y=y)
+    ex.gemm(x, w, sign, scale, K, workspace=ws, y=y, codebook=codebook)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
-        ex.gemm(x, w, sign, scale, K, workspace=ws, y=y)
+        ex.gemm(x, w, sign, scale, K, workspace=ws, y=y, codebook=codebook)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
@@ -368,6 +369,17 @@ def main():
         extra["gemm_m2048_8192x8192_k4"] = {"tflops": round(tf, 1), "ms": round(gms, 3),
                                             "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
         extra["llama70b_m1"] = llama70b_rates(torch, ex)
+        # the byte-sum (dp4a) codebook on the K=4 MLP launches and the GEMM
+        calls = build_mlp(torch, ex, 1, Ks=(4,), replicas=args.replicas)
+        for c in calls:
+            c["codebook"] = 1
+        kd1 = per_kernel_events(torch, ex, calls, args.replicas, 20)
+        tf1, gms1 = gemm_tflops(torch, ex, codebook=1)
+        extra["codebook1"] = {c["name"]: {"us": round(1e3 * kd1[c["name"]], 2),
+                                          "gbs": round(c["bytes"] / (kd1[c["name"]] * 1e-3) / 1e9, 1)} for c in calls}
+        extra["codebook1"]["gemm_m2048_8192x8192_k4"] = {"tflops": round(tf1, 1), "ms": round(gms1, 3)}
+        del calls
+        torch.cuda.empty_cache()
         extra["llama8b_stack_m1"] = {"fused": stack_tokens_per_s(torch, ex, True),
                                      "unfused": stack_tokens_per_s(torch, ex, False)}
 
