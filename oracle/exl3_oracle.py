@@ -342,3 +342,143 @@ def y_scalar(x, trellis, sign, out_scale, K: int, r: int, o: int, cb: int = 0) -
 def fp16_bits(a: np.ndarray) -> np.ndarray:
     """View fp16 values as their uint16 bit patterns (for bit-exact comparison)."""
     return np.asarray(a, dtype=np.float16).view(np.uint16)
+
+
+# ---------------------------------------------------------------------------
+# Encoding: the tail-biting Viterbi search ("ExLlamaV3 inference speed", section
+# "Viterbi encoding kernel": each 16x16 block is one codeword found by a forward
+# Viterbi pass over the trellis, keeping the accumulated cost of every edge and
+# the minimum-cost path; the tail-biting boundary is closed by enumerating start
+# states so that the codeword's head and tail agree).
+#
+# Trellis: an L-bit state; state i+1 = (state i >> K) | (b << (L - K)) for the K
+# new bits b.  So the predecessors of s are the 2^K states (u << K) | j with
+# u = s & (2^(L-K) - 1), and one step is
+#     M[u]     = min_j cost[(u << K) | j]     (the first j on ties)
+#     cost'[s] = M[s & (2^(L-K) - 1)] + (w_i - value[s])^2.
+# Decisions are taken in float32 with the subtraction, the square and the sum
+# each rounded (no fused multiply-add), so a GPU encoder can match them bit
+# for bit.  A stream is tail-biting when state T-1's top L-K bits equal state
+# 0's low L-K bits (the window wraps at the end of the stream).
+# ---------------------------------------------------------------------------
+def trellis_viterbi(w, values, L: int, K: int, v=None):
+    """Minimum-cost state path for targets w [T] over codebook values [2^L].
+
+    v None: free start and end.  v given: start states with low L-K bits == v
+    and end states with high L-K bits == v (a tail-biting path).
+    Returns (path int64 [T], cost float32).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    values = np.asarray(values, dtype=np.float32)
+    T, S = w.shape[0], 1 << L
+    low = (1 << (L - K)) - 1
+    s = np.arange(S, dtype=np.int64)
+
+    def err(i):
+        d = np.float32(w[i]) - values          # float32 subtract
+        return d * d                            # float32 square
+
+    cost = err(0)
+    if v is not None:
+        cost = np.where((s & low) == v, cost, np.float32(np.inf)).astype(np.float32)
+    back = np.empty((T, low + 1), dtype=np.int64)
+    for i in range(1, T):
+        blocks = cost.reshape(low + 1, 1 << K)
+        j = np.argmin(blocks, axis=1)            # first minimum on ties
+        M = blocks[np.arange(low + 1), j]
+        back[i] = j
+        cost = (M[s & low] + err(i)).astype(np.float32)
+    if v is None:
+        end = int(np.argmin(cost))
+    else:
+        cand = (v << K) + np.arange(1 << K)
+        end = int(cand[np.argmin(cost[cand])])
+    path = np.empty(T, dtype=np.int64)
+    path[T - 1] = end
+    for i in range(T - 1, 0, -1):
+        u = path[i] & low
+        path[i - 1] = (u << K) | back[i][u]
+    return path, np.float32(cost[end])
+
+
+def tail_biting_exact(w, values, L: int, K: int):
+    """Optimal tail-biting path: the best of the constrained searches over every
+    value of the L-K overlap bits (the full enumeration of start states)."""
+    best = None
+    for v in range(1 << (L - K)):
+        path, c = trellis_viterbi(w, values, L, K, v)
+        if best is None or c < best[1]:
+            best = (path, c)
+    return best
+
+
+def tail_biting_two_pass(w, values, L: int, K: int):
+    """The encoder's search: a free pass over the targets rotated by T/2 picks
+    the overlap bits (the low L-K bits of its state at the original position
+    0), then one constrained pass returns a tail-biting path with them."""
+    w = np.asarray(w, dtype=np.float32)
+    T = w.shape[0]
+    h = T // 2
+    path_r, _ = trellis_viterbi(np.roll(w, -h), values, L, K)
+    v = int(path_r[T - h] & ((1 << (L - K)) - 1))
+    return trellis_viterbi(w, values, L, K, v)
+
+
+def path_cost(w, values, path) -> np.float32:
+    """Cost of a path with the search's float32 rounding and summation order."""
+    w = np.asarray(w, dtype=np.float32)
+    values = np.asarray(values, dtype=np.float32)
+    c = np.float32(0)
+    for i, s in enumerate(path):
+        d = np.float32(w[i]) - values[s]
+        c = np.float32(c + np.float32(d * d)) if i else np.float32(d * d)
+    return c
+
+
+def pack_path(path, K: int) -> np.ndarray:
+    """Tile stream of a tail-biting path of 256 states: stream bits [iK, iK+K)
+    are the low K bits of state i (FMT-3, FMT-4), as 16K uint16 words."""
+    path = np.asarray(path, dtype=np.int64)
+    assert path.shape == (256,)
+    bits = ((path[:, None] >> np.arange(K)[None, :]) & 1).reshape(-1)  # stream bit iK + b
+    return np.packbits(bits.astype(np.uint8), bitorder="little").view("<u2").astype(np.uint16)
+
+
+def encode_tile(w, K: int, cb: int = 0):
+    """Encode one tile (256 targets in trellis order, float32) at K bits per
+    weight: the two-pass tail-biting search over the 16-bit trellis with the
+    codebook's values.  Returns (words uint16 [16K], cost float32)."""
+    _check_k(K)
+    values = codebook(np.arange(65536), cb).astype(np.float32)
+    path, cost = tail_biting_two_pass(np.asarray(w, np.float32).reshape(256), values, 16, K)
+    return pack_path(path, K), cost
+
+
+def encode_tiles(W, K: int, cb: int = 0):
+    """encode_tile over [n, 256] targets: (words [n, 16K], costs [n])."""
+    W = np.asarray(W, dtype=np.float32).reshape(-1, 256)
+    out = np.empty((W.shape[0], 16 * K), dtype=np.uint16)
+    costs = np.empty(W.shape[0], dtype=np.float32)
+    for t in range(W.shape[0]):
+        out[t], costs[t] = encode_tile(W[t], K, cb)
+    return out, costs
+
+
+def brute_force_tail_biting(w, values, L: int, K: int):
+    """Minimum cost over every cyclic stream of T*K bits (tiny T*K only): state
+    i is the L-bit window at bit iK, wrapping at the end (pure Python)."""
+    w = [float(np.float32(x)) for x in w]
+    T = len(w)
+    n = T * K
+    best = None
+    for stream in range(1 << n):
+        path = []
+        for i in range(T):
+            st = 0
+            for b in range(L):
+                st |= ((stream >> ((i * K + b) % n)) & 1) << b
+            path.append(st)
+        c = path_cost(w, values, path)
+        if best is None or c < best[1]:
+            best = (path, c)
+    return best
