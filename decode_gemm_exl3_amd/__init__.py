@@ -20,7 +20,8 @@ import ctypes
 import os
 
 __all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemv_multi",
-           "gemm", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg"]
+           "gemm", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg", "encode_slot_bytes",
+           "encode_tiles"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -69,6 +70,10 @@ def load() -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.exl3_gemv_multi.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(_Proj), i32, vp, sz, vp]
     lib.exl3_gemv_multi.restype = ctypes.c_int
+    lib.exl3_encode_slot_bytes.argtypes = [i32]
+    lib.exl3_encode_slot_bytes.restype = i64
+    lib.exl3_encode_tiles.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
+    lib.exl3_encode_tiles.restype = ctypes.c_int
     lib.exl3_status_string.argtypes = [ctypes.c_int]
     lib.exl3_status_string.restype = ctypes.c_char_p
     _LIB = lib
@@ -174,6 +179,35 @@ def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None
                                 _stream(stream))
     _check(rc, "exl3_gemv_multi")
     return ys
+
+
+def encode_slot_bytes(bits: int, codebook: int = 0) -> int:
+    """Workspace bytes of exl3_encode_tiles per tile in flight."""
+    n = int(load().exl3_encode_slot_bytes(bits_arg(bits, codebook)))
+    if n < 0:
+        _check(n, "exl3_encode_slot_bytes")
+    return n
+
+
+def encode_tiles(w, bits: int, codebook: int = 0, workspace=None, words=None, costs=None, slots: int = 256,
+                 stream=None):
+    """Quantise fp32 tiles [T, 256] to trellis streams: returns (words [T, 16K] int16, costs [T] fp32).
+
+    workspace: a uint8 device tensor; by default `slots` tiles in flight.
+    """
+    import torch
+    T = w.shape[0]
+    if words is None:
+        words = torch.empty((T, 16 * bits), dtype=torch.int16, device=w.device)
+    if costs is None:
+        costs = torch.empty((T,), dtype=torch.float32, device=w.device)
+    if workspace is None:
+        workspace = torch.empty(encode_slot_bytes(bits, codebook) * max(1, min(slots, T)), dtype=torch.uint8,
+                                device=w.device)
+    rc = load().exl3_encode_tiles(_ptr(w), T, bits_arg(bits, codebook), _ptr(words), _ptr(costs), _ptr(workspace),
+                                  workspace.numel(), _stream(stream))
+    _check(rc, "exl3_encode_tiles")
+    return words, costs
 
 
 def gemm(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):

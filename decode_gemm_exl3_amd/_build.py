@@ -7,7 +7,7 @@ import subprocess
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libexl3.so")
-SOURCES = ["exl3_api.hip", "exl3_kernels.hip", "exl3_gemm.hip"]
+SOURCES = ["exl3_api.hip", "exl3_kernels.hip", "exl3_gemm.hip", "exl3_encode.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -234,6 +234,33 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
 }
 
+int64_t exl3_encode_slot_bytes(int32_t bits) {
+    if (bad_bits(bits)) return EXL3_EINVAL;
+    return exl3::encode_slot_bytes(k_of(bits));
+}
+
+int exl3_encode_tiles(const float* w, int64_t n_tiles, int32_t bits, uint16_t* words, float* costs,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (bad_bits(bits) || n_tiles < 0) return EXL3_EINVAL;
+    if (n_tiles == 0) return EXL3_OK;
+    if (!w || !words) return EXL3_EINVAL;
+    const int64_t slot = exl3::encode_slot_bytes(k_of(bits));
+    if (!workspace || (int64_t)workspace_bytes < slot) return EXL3_EWORKSPACE;
+    int64_t slots = (int64_t)workspace_bytes / slot;
+    const int64_t cap = (int64_t)cu_count() * 4;  // tiles in flight: a few per CU
+    if (slots > cap) slots = cap;
+    if (slots > n_tiles) slots = n_tiles;
+    exl3::EncodeParams p;
+    p.w = w;
+    p.n_tiles = n_tiles;
+    p.words = words;
+    p.costs = costs;
+    p.scratch = static_cast<uint8_t*>(workspace);
+    p.slot_bytes = slot;
+    const hipError_t e = exl3::launch_encode(k_of(bits), cb_of(bits), p, (int)slots, (hipStream_t)stream);
+    return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+}
+
 const char* exl3_status_string(int status) {
     switch (status) {
         case EXL3_OK: return "ok";

@@ -46,6 +46,19 @@ struct GemmParams {
     int tiles_in, n_strips;
 };
 
+// The encoder: targets fp32 [n_tiles][256] (trellis order) -> words [n_tiles][16K]
+// and the cost of each tile; scratch holds one slot of slot_bytes per workgroup.
+struct EncodeParams {
+    const float* w;
+    int64_t n_tiles;
+    uint16_t* words;
+    float* costs;  // may be null
+    uint8_t* scratch;
+    int64_t slot_bytes;
+};
+inline int64_t encode_slot_bytes(int K) { return (int64_t)256 << (16 - K); }
+hipError_t launch_encode(int K, int cb, const EncodeParams& p, int grid, hipStream_t s);
+
 // cb selects the codebook: 0 (multiply, mask-and-plant, half sum) or 1 (byte sum)
 hipError_t launch_decode(int K, int cb, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s);
 hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr,

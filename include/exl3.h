@@ -154,6 +154,38 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
               uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * exl3_encode_slot_bytes: workspace bytes exl3_encode_tiles needs per tile in
+ * flight (256 * 2^(16-K): the choice of every trellis step), or EXL3_EINVAL for
+ * a bad bits argument.  Host-only.
+ */
+int64_t exl3_encode_slot_bytes(int32_t bits);
+
+/*
+ * exl3_encode_tiles: quantise tiles to trellis streams (pages: "Viterbi encoding
+ * kernel": one thread block per 16x16 block of 256 weights, a forward Viterbi
+ * pass that keeps the accumulated cost of every edge and takes the
+ * minimum-cost path, the tail-biting boundary closed over the start states so
+ * that the codeword's head and tail agree; instances per (K, codebook)).
+ *   w         : fp32 [n_tiles][256] targets, element i of a tile = row i/16,
+ *               column i%16 (the format's tile order), device.
+ *   words     : uint16 [n_tiles][16*K] output streams in the format above, device.
+ *   costs     : fp32 [n_tiles] sum of squared errors of each tile, device, or NULL.
+ *   workspace : at least exl3_encode_slot_bytes(bits) bytes; more lets more
+ *               tiles run at once.  Contents need no initialisation.
+ * The search: state i+1 = (state i >> K) | (b << (16-K)); a step keeps, for every
+ * state, the cheapest predecessor (first on ties) and adds (w_i - c(state))^2,
+ * each operation rounded in fp32 with no fused multiply-add.  A free pass over
+ * the targets rotated by 128 fixes the 16-K overlap bits (the low bits of its
+ * state at position 0); a second pass starts in the states with those low bits
+ * and ends in those whose top bits equal them, so every stream is a valid
+ * tail-biting walk.  The result is deterministic.  n_tiles == 0 is a no-op;
+ * EXL3_EINVAL for null w or words, n_tiles < 0 or a bad bits argument;
+ * EXL3_EWORKSPACE for a workspace below one slot.
+ */
+int exl3_encode_tiles(const float* w, int64_t n_tiles, int32_t bits, uint16_t* words, float* costs,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Text for a status code (static storage; never NULL). */
 const char* exl3_status_string(int status);
 

@@ -29,7 +29,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemv_multi", "exl3_gemm",
-                          "exl3_status_string"}
+                          "exl3_encode_slot_bytes", "exl3_encode_tiles", "exl3_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -137,6 +137,21 @@ def test_gemv_multi_argument_errors(lib):
     assert _multi_call(lib, [(11, 12, 13, 16, 0), (21, 22, 13, 16, 0)]) == -1  # same y twice
     assert _multi_call(lib, good, m=0, x=None, sg=None) == 0     # m == 0 is a no-op
     assert _multi_call(lib, [(11, 12, 13, 65536, 0)], n_in=65536) == -2  # >= 2 GiB of weights
+
+
+def test_encode_sizes_and_argument_errors(lib):
+    for K in range(1, 9):
+        assert lib.exl3_encode_slot_bytes(K) == 256 * (1 << (16 - K))
+        assert lib.exl3_encode_slot_bytes(K | ex.CODEBOOK_BYTE_SUM) == 256 * (1 << (16 - K))
+    assert lib.exl3_encode_slot_bytes(0) == -1 and lib.exl3_encode_slot_bytes(9) == -1
+    big = 1 << 30
+    assert lib.exl3_encode_tiles(1, 1, 0, 2, None, 3, big, None) == -1       # bad bits
+    assert lib.exl3_encode_tiles(1, -1, 4, 2, None, 3, big, None) == -1      # n_tiles < 0
+    assert lib.exl3_encode_tiles(None, 1, 4, 2, None, 3, big, None) == -1
+    assert lib.exl3_encode_tiles(1, 1, 4, None, None, 3, big, None) == -1
+    assert lib.exl3_encode_tiles(1, 1, 4, 2, None, None, big, None) == -3    # no workspace
+    assert lib.exl3_encode_tiles(1, 1, 4, 2, None, 3, 1000, None) == -3      # below one slot
+    assert lib.exl3_encode_tiles(None, 0, 4, None, None, None, 0, None) == 0  # no tiles: no-op
 
 
 def test_decode_tile_argument_errors(lib):
