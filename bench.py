@@ -291,6 +291,30 @@ def llama70b_rates(torch, ex, replicas=3, steps=20):
     return out
 
 
+def encode_rates(torch, ex, n_tiles=2048, Ks=(2, 3, 4)):
+    """Tail-biting Viterbi encoder: tiles/s on unit-Gaussian tiles and the mean
+    squared error per weight it reaches."""
+    out = {}
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(5)
+    for K in Ks:
+        w = torch.randn((n_tiles, 256), device="cuda", generator=gen)
+        ws = torch.empty(ex.encode_slot_bytes(K) * min(n_tiles, 1024), dtype=torch.uint8, device="cuda")
+        ex.encode_tiles(w[:64], K, workspace=ws)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _, costs = ex.encode_tiles(w, K, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        out[f"k{K}"] = {"tiles_per_s": round(n_tiles / ms * 1e3), "mse": round(float(costs.mean()) / 256, 5),
+                        "s_per_4096x4096": round(65536 / n_tiles * ms / 1e3, 3)}
+        del w, ws
+    return out
+
+
 def only_mode(what, steps, replicas):
     """Short runs for the profiler: the fused gate+up launch at K=4 alone (the
     dominant kernel), or a plain copy of known size."""
@@ -369,6 +393,7 @@ def main():
         extra["gemm_m2048_8192x8192_k4"] = {"tflops": round(tf, 1), "ms": round(gms, 3),
                                             "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
         extra["llama70b_m1"] = llama70b_rates(torch, ex)
+        extra["encode"] = encode_rates(torch, ex)
         # the byte-sum (dp4a) codebook on the K=4 MLP launches and the GEMM
         calls = build_mlp(torch, ex, 1, Ks=(4,), replicas=args.replicas)
         for c in calls:
