@@ -20,12 +20,13 @@ import ctypes
 import os
 
 __all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemv_multi",
-           "gemm", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg", "encode_slot_bytes",
+           "gemm", "linear", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg", "encode_slot_bytes",
            "encode_tiles"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 MAX_PROJ = 4  # EXL3_GEMV_MAX_PROJ
+GEMV_MAX_M = 16  # EXL3_GEMV_MAX_M
 CODEBOOK_BYTE_SUM = 0x100  # EXL3_CODEBOOK_BYTE_SUM: flag in the bits argument selecting codebook 1
 
 
@@ -64,7 +65,7 @@ def load() -> ctypes.CDLL:
     lib.exl3_pack_info.restype = ctypes.c_int
     lib.exl3_decode_tile.argtypes = [vp, i32, i64, vp, vp]
     lib.exl3_decode_tile.restype = ctypes.c_int
-    for name in ("exl3_gemv", "exl3_gemm"):
+    for name in ("exl3_gemv", "exl3_gemm", "exl3_linear"):
         f = getattr(lib, name)
         f.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         f.restype = ctypes.c_int
@@ -155,12 +156,12 @@ def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=N
 
 
 def gemv(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):
-    """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 8 (fp16 out)."""
+    """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 16 (fp16 out)."""
     return _linear("exl3_gemv", x, trellis, sign, out_scale, bits, workspace, y, stream, codebook)
 
 
 def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None, codebook: int = 0):
-    """One launch for several projections of the same x (1 <= m <= 8).
+    """One launch for several projections of the same x (1 <= m <= 16).
 
     weights: sequence of (trellis, out_scale) pairs sharing n_in and bits; the
     same sign vector applies to all.  Returns the list of y, fp16 [m, n_out_i].
@@ -179,6 +180,11 @@ def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None
                                 _stream(stream))
     _check(rc, "exl3_gemv_multi")
     return ys
+
+
+def linear(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):
+    """Any m >= 1: the GEMV or the GEMM, as the library's measured table picks."""
+    return _linear("exl3_linear", x, trellis, sign, out_scale, bits, workspace, y, stream, codebook)
 
 
 def encode_slot_bytes(bits: int, codebook: int = 0) -> int:

@@ -34,13 +34,32 @@ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 // Workspace needs.  Nothing in the workspace survives between calls, so each
 // call lays out only what it uses from offset 0:
 //   gemv: nothing (one kernel, partial sums stay in LDS);
-//   gemm: the rotated input, fp16 [m][n_in].
 int64_t gemv_ws_bytes(int n_out, int m) { (void)n_out; (void)m; return 0; }
-int64_t gemm_ws_bytes(int n_in, int m) { return align256((int64_t)m * n_in * 2); }
+//   gemm: the rotated input, fp16 [m][n_in], then for a split input dimension
+//         the fp32 partial sums [zsplit][m][n_out].
+int64_t gemm_rot_bytes(int n_in, int m) { return align256((int64_t)m * n_in * 2); }
+int64_t gemm_ws_bytes(int n_in, int n_out, int m, int cus) {
+    int z = 1, kz = 0;
+    exl3::plan_gemm_split(m, n_out, n_in / 16, cus, &z, &kz);
+    return gemm_rot_bytes(n_in, m) + (z > 1 ? align256((int64_t)z * m * n_out * 4) : 0);
+}
 int64_t ws_total(int n_in, int n_out, int max_m) {
-    const int64_t a = gemv_ws_bytes(n_out, max_m < 8 ? max_m : 8);
-    const int64_t b = gemm_ws_bytes(n_in, max_m);
-    return a > b ? a : b;
+    int64_t best = gemv_ws_bytes(n_out, max_m < EXL3_GEMV_MAX_M ? max_m : EXL3_GEMV_MAX_M);
+    // the split depends on m through the number of 256-row blocks: the largest
+    // m of each block count needs the most; past the counts that split, the
+    // rotated input of max_m rows is all
+    for (int64_t b = 1; b * exl3::GEMM_BM < (int64_t)max_m + exl3::GEMM_BM; ++b) {
+        const int m = (int)(b * exl3::GEMM_BM < max_m ? b * exl3::GEMM_BM : max_m);
+        const int64_t need = gemm_ws_bytes(n_in, n_out, m, exl3::GEMM_SIZING_CUS);
+        if (need > best) best = need;
+        int z = 1, kz = 0;
+        exl3::plan_gemm_split(m, n_out, n_in / 16, exl3::GEMM_SIZING_CUS, &z, &kz);
+        if (z == 1) {
+            const int64_t all = gemm_rot_bytes(n_in, max_m);
+            return all > best ? all : best;
+        }
+    }
+    return best;
 }
 
 // GEMV launch plan.  Persistent workgroups (about one per CU) own strips
@@ -149,7 +168,7 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
                     void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    if (m < 0 || m > 8 || bad_bits(bits) || n_in <= 0 || (n_in % 128) != 0) return EXL3_EINVAL;
+    if (m < 0 || m > EXL3_GEMV_MAX_M || bad_bits(bits) || n_in <= 0 || (n_in % 128) != 0) return EXL3_EINVAL;
     if (!proj || n_proj < 1 || n_proj > EXL3_GEMV_MAX_PROJ) return EXL3_EINVAL;
     for (int i = 0; i < n_proj; ++i) {
         const int32_t n_out = proj[i].n_out;
@@ -195,7 +214,7 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
 int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
               void* workspace, size_t workspace_bytes, void* stream) {
-    if (m > 8) return EXL3_EINVAL;
+    if (m > EXL3_GEMV_MAX_M) return EXL3_EINVAL;
     const int mm = m > 0 ? m : 1;
     int rc = common_checks(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes,
                            gemv_ws_bytes(n_out, mm));
@@ -213,10 +232,30 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
               void* workspace, size_t workspace_bytes, void* stream) {
     int rc = common_checks(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes,
-                           gemm_ws_bytes(n_in, m > 0 ? m : 1));
+                           gemm_rot_bytes(n_in, m > 0 ? m : 1));
     if (rc <= 0) return rc;
     if ((int64_t)m > (int64_t)65535 * 64) return EXL3_EUNSUPPORTED;
     uint16_t* xr = static_cast<uint16_t*>(workspace);
+    // split the input dimension while the output blocks leave CUs idle, as far
+    // as the workspace holds the partial sums (no split needs none)
+    static const int z_force = env_int("EXL3_GEMM_SPLIT", 0);
+    int zsplit = 1, kz = n_in / 16;
+    exl3::plan_gemm_split(m, n_out, n_in / 16, z_force > 0 ? z_force * 1000000 : cu_count(), &zsplit, &kz);
+    if (z_force > 0 && zsplit > z_force) {
+        const int steps = n_in / 64, kstep = (steps + z_force - 1) / z_force;
+        kz = 4 * kstep;
+        zsplit = (steps + kstep - 1) / kstep;
+    }
+    const int64_t rot = gemm_rot_bytes(n_in, m);
+    while (zsplit > 1 && rot + align256((int64_t)zsplit * m * n_out * 4) > (int64_t)workspace_bytes) {
+        const int steps = n_in / 64, z = zsplit - 1, kstep = (steps + z - 1) / z;
+        kz = 4 * kstep;
+        zsplit = (steps + kstep - 1) / kstep;
+    }
+    if (zsplit <= 1) {
+        zsplit = 1;
+        kz = n_in / 16;
+    }
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = exl3::launch_rotate(x, sign, m, n_in, xr, s);
     if (e != hipSuccess) return EXL3_EHIP;
@@ -230,8 +269,22 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
     p.n_out = n_out;
     p.tiles_in = n_in / 16;
     p.n_strips = n_out / 16;
+    p.zsplit = zsplit;
+    p.kz = kz;
+    p.part = zsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + rot) : nullptr;
     e = exl3::launch_gemm(k_of(bits), cb_of(bits), p, s);
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
+}
+
+int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+                const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    // Measured crossover (MI355X, K = 2 and 4; 4096->14336, 14336->4096, 4096->4096):
+    // the GEMV wins while x' of the m rows (4 bytes per input, duplicated fp16)
+    // stays near one LDS chunk, i.e. m * n_in <= 2^17; past it the split GEMM does.
+    const bool use_gemv = m <= EXL3_GEMV_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
+    return use_gemv ? exl3_gemv(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream)
+                    : exl3_gemm(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream);
 }
 
 int64_t exl3_encode_slot_bytes(int32_t bits) {

@@ -26,8 +26,8 @@
 
 namespace exl3 {
 
-constexpr int GM_BM = 256;
-constexpr int GM_BN = 256;            // 16 strips, 64 outputs per wave
+constexpr int GM_BM = GEMM_BM;
+constexpr int GM_BN = GEMM_BN;        // 16 strips, 64 outputs per wave
 constexpr int GM_BK = 64;             // 4 tile columns
 constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 bytes)
 constexpr int GM_A_HALVES = GM_BM * GM_LD;
@@ -50,6 +50,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
     const int m0 = (lin / nbx) * GM_BM;
     const int s0 = (lin % nbx) * (GM_BN / 16) + 4 * nq;  // first strip of this wave
+    // this workgroup's tile columns (split-k): [t0, t1)
+    const int t0 = blockIdx.z * p.kz;
+    const int t1 = min(p.tiles_in, t0 + p.kz);
     const CbRegs cr = cb_regs<CB>();
 
     // ---- weights: fragment j = strip s0 + j, tile column 2 mh + (g >> 1) of the
@@ -142,13 +145,13 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], b[j], acc[i][j], 0, 0, 0);
     };
 
-    // ---- prologue: step 0 decoded and staged
+    // ---- prologue: step t0 decoded and staged
 #pragma unroll
-    for (int j = 0; j < 4; ++j) load_frag(j, 0);
-    load_a(0);
-    decode_step(4, 0);
+    for (int j = 0; j < 4; ++j) load_frag(j, t0);
+    load_a(t0);
+    decode_step(t0 + 4, 0);
     store_a(0);
-    load_a(4);
+    load_a(t0 + 4);
     __syncthreads();
 
     // One copy of the main loop per partner, with its phase fixed at compile
@@ -159,7 +162,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     auto main_loop = [&](auto phase) {
         constexpr int MH = decltype(phase)::value;
         int buf = 0;
-        for (int tc = 0; tc < p.tiles_in; tc += 4, buf ^= 1) {
+        for (int tc = t0; tc < t1; tc += 4, buf ^= 1) {
             // the next step's x' goes to the other buffer: its last readers were
             // in the previous step, before this step's barrier
             store_a(buf ^ 1);
@@ -181,6 +184,22 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     else
         main_loop(std::integral_constant<int, 1>{});
     // D[4g + r][n] of fragment (i, j): row 128 mh + 16i + 4g + r, output 16 (s0 + j) + n
+    if (p.zsplit > 1) {  // fp32 partial sums of this split; the reduction scales them
+        float* part = p.part + (int64_t)blockIdx.z * p.m * p.n_out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int o = (s0 + j) * 16 + n;
+            if (o >= p.n_out) continue;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + 128 * mh + i * 16 + 4 * g + r;
+                    if (row < p.m) part[(int64_t)row * p.n_out + o] = acc[i][j][r];
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int o = (s0 + j) * 16 + n;
@@ -196,10 +215,42 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
+// Split-k reduction: y[r][o] = fp16(out_scale[o] * 128 * sum_z part[z][r][o]),
+// the splits added in order.  Four outputs per thread (n_out % 16 == 0).
+__global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part,
+                                                          const uint16_t* __restrict__ out_scale,
+                                                          uint16_t* __restrict__ y, int m, int n_out, int zsplit) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // group of 4 outputs
+    const int64_t total = (int64_t)m * n_out / 4;
+    if (q >= total) return;
+    const int64_t e = 4 * q;
+    const int o = (int)(e % n_out);
+    const int64_t plane = (int64_t)m * n_out;
+    float4 v = *reinterpret_cast<const float4*>(part + e);
+    for (int z = 1; z < zsplit; ++z) {
+        const float4 w = *reinterpret_cast<const float4*>(part + z * plane + e);
+        v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    const float a[4] = {v.x, v.y, v.z, v.w};
+    uint16_t out[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float sc = __half2float(__ushort_as_half(out_scale[o + t])) * 128.0f;
+        out[t] = __half_as_ushort(__float2half_rn(sc * a[t]));
+    }
+    *reinterpret_cast<uint2*>(y + e) = uint2{(uint32_t)out[0] | ((uint32_t)out[1] << 16),
+                                           (uint32_t)out[2] | ((uint32_t)out[3] << 16)};
+}
+
 template <int K, int CB>
 static hipError_t launch_gemm_k(const GemmParams& p, hipStream_t s) {
-    dim3 grid((p.n_strips + 15) / 16, (p.m + GM_BM - 1) / GM_BM);
+    dim3 grid((p.n_strips + 15) / 16, (p.m + GM_BM - 1) / GM_BM, p.zsplit);
     hipLaunchKernelGGL((gemm_kernel<K, CB>), grid, dim3(512), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.zsplit <= 1) return e;
+    const int64_t groups = (int64_t)p.m * p.n_out / 4;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s, p.part,
+                       p.out_scale, p.y, p.m, p.n_out, p.zsplit);
     return hipGetLastError();
 }
 

@@ -44,7 +44,30 @@ struct GemmParams {
     uint16_t* y;
     int m, n_in, n_out;
     int tiles_in, n_strips;
+    // split-k: zsplit workgroups share an output block, each over kz tile
+    // columns of the input; with zsplit > 1 they write fp32 partial sums
+    // part[z][m][n_out] and a reduction forms y
+    int zsplit, kz;
+    float* part;
 };
+
+constexpr int GEMM_BM = 256, GEMM_BN = 256;  // output block of one GEMM workgroup
+constexpr int GEMM_MAX_SPLIT = 16;
+constexpr int GEMM_SIZING_CUS = 256;         // CU count the workspace is sized for (MI355X)
+
+// Split-k plan: split the input dimension while the output blocks alone would
+// leave CUs idle (a medium m gives few blocks), in multiples of 4 tile columns.
+inline void plan_gemm_split(int m, int n_out, int tiles_in, int cus, int* zsplit, int* kz) {
+    const int blocks = ((n_out / 16 + 15) / 16) * ((m + GEMM_BM - 1) / GEMM_BM);
+    int z = blocks >= cus ? 1 : (cus + blocks - 1) / blocks;
+    const int steps = tiles_in / 4;
+    if (z > GEMM_MAX_SPLIT) z = GEMM_MAX_SPLIT;
+    if (z > steps) z = steps;
+    if (z < 1) z = 1;
+    const int kstep = (steps + z - 1) / z;  // steps per split
+    *kz = 4 * kstep;
+    *zsplit = (steps + kstep - 1) / kstep;
+}
 
 // The encoder: targets fp32 [n_tiles][256] (trellis order) -> words [n_tiles][16K]
 // and the cost of each tile; scratch holds one slot of slot_bytes per workgroup.

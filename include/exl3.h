@@ -96,9 +96,12 @@ int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m,
 int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
                      uint16_t* out, void* stream);
 
+/* Largest m the GEMV calls take (the rows of one matrix-core tile). */
+#define EXL3_GEMV_MAX_M 16
+
 /*
- * exl3_gemv: the decode-matmul for 1 <= m <= 8 (pages: "small-batch GEMV",
- * where small m makes the weight stream the bottleneck).
+ * exl3_gemv: the decode-matmul for 1 <= m <= EXL3_GEMV_MAX_M (pages: "small-batch
+ * GEMV", where small m makes the weight stream the bottleneck).
  *   x         : fp16 [m][n_in]
  *   trellis   : uint16 [n_out/16][n_in/16][16*K]
  *   sign      : fp16 [n_in], entries +-1
@@ -108,7 +111,7 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
  *               bytes for max_m >= m.  Its contents need no initialisation and
  *               are meaningless after the call.  Calls that may run at the same
  *               time (different streams) need separate workspaces.
- * m == 0 is a no-op.  m > 8 or m < 0 gives EXL3_EINVAL (use exl3_gemm).
+ * m == 0 is a no-op.  m > EXL3_GEMV_MAX_M or m < 0 gives EXL3_EINVAL (use exl3_gemm).
  */
 int exl3_gemv(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
@@ -138,7 +141,7 @@ typedef struct exl3_proj_t {
  *                            The y buffers must not overlap each other or x.
  *   workspace              : as exl3_gemv (the GEMV needs none today).
  * Each proj[i].y equals what exl3_gemv gives for that projection, up to fp32
- * summation order.  m == 0 is a no-op.  EXL3_EINVAL for m outside 0..8, n_proj
+ * summation order.  m == 0 is a no-op.  EXL3_EINVAL for m outside 0..EXL3_GEMV_MAX_M, n_proj
  * outside 1..EXL3_GEMV_MAX_PROJ, a null pointer, a bad shape or two identical y.
  */
 int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t n_in, int32_t bits,
@@ -146,13 +149,30 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
                     void* stream);
 
 /*
- * exl3_gemm: the same result for any m >= 1, built for m >= 16 (pages: "GEMM
+ * exl3_gemm: the same result for any m >= 1, built for larger m (pages: "GEMM
  * kernel", where the Hadamard rotation of the input and the decode are fused
- * with a tiled matrix product).  Arguments and workspace rules as exl3_gemv.
+ * with a tiled matrix product).  Arguments and workspace rules as exl3_gemv;
+ * the workspace holds the rotated input and, when the input dimension is split
+ * across workgroups (few output blocks), fp32 partial sums: a workspace of the
+ * size exl3_pack_info gives always suffices, a smaller one (at least m*n_in*2
+ * bytes, rounded up to 256) splits less.
  */
 int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
               uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * exl3_linear: the same result for any m >= 1, through exl3_gemv or exl3_gemm as
+ * a measured table picks (pages: "GEMM kernel" - the kernel map chooses tile
+ * sizes and concurrency by architecture and shape; "small-batch GEMV" - small m
+ * goes to the GEMV).  The GEMV serves m <= 16 while m * n_in <= 2^17, the GEMM
+ * (with its input dimension split across workgroups when the output blocks
+ * alone leave compute units idle) the rest.  Arguments and workspace as
+ * exl3_gemm.
+ */
+int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+                const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
+                uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * exl3_encode_slot_bytes: workspace bytes exl3_encode_tiles needs per tile in

@@ -29,7 +29,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemv_multi", "exl3_gemm",
-                          "exl3_encode_slot_bytes", "exl3_encode_tiles", "exl3_status_string"}
+                          "exl3_linear", "exl3_encode_slot_bytes", "exl3_encode_tiles", "exl3_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -80,7 +80,7 @@ def _gemv_call(lib, fn, x=1, m=1, tr=1, sg=1, sc=1, n_in=128, n_out=16, bits=4, 
     return getattr(lib, fn)(x, m, tr, sg, sc, n_in, n_out, bits, y, ws, wsb, None)
 
 
-@pytest.mark.parametrize("fn", ["exl3_gemv", "exl3_gemm"])
+@pytest.mark.parametrize("fn", ["exl3_gemv", "exl3_gemm", "exl3_linear"])
 def test_linear_argument_errors_return_before_launch(lib, fn):
     # every case is rejected on the host, so fake non-null pointers are never used
     assert _gemv_call(lib, fn, m=-1) == -1
@@ -103,10 +103,20 @@ def test_gemm_workspace_errors(lib):
     # gemm stages the rotated input in the workspace; gemv needs none
     assert _gemv_call(lib, "exl3_gemm", ws=None) == -3
     assert _gemv_call(lib, "exl3_gemm", wsb=16) == -3
+    # exl3_linear sends large m to the GEMM
+    assert _gemv_call(lib, "exl3_linear", m=64, ws=None) == -3
 
 
-def test_gemv_rejects_m_above_8(lib):
-    assert _gemv_call(lib, "exl3_gemv", m=9) == -1
+def test_pack_info_workspace_covers_split_partials(lib):
+    # few output blocks (medium m) split the input dimension: the workspace
+    # holds the rotated input and fp32 partial sums of up to 16 splits
+    info = ex.pack_info(4096, 4096, 4, 256)
+    assert info["workspace_bytes"] >= 256 * 4096 * 2 + 16 * 256 * 4096 * 4
+    assert ex.pack_info(8192, 8192, 4, 2048)["workspace_bytes"] >= 2048 * 8192 * 2
+
+
+def test_gemv_rejects_m_above_16(lib):
+    assert _gemv_call(lib, "exl3_gemv", m=17) == -1
 
 
 def _multi_call(lib, projs, x=1, m=1, sg=1, n_in=128, bits=4, n_proj=None):
@@ -119,7 +129,7 @@ def test_gemv_multi_argument_errors(lib):
     # (trellis, out_scale, y, n_out, reserved); fake pointers, never dereferenced
     good = [(11, 12, 13, 16, 0), (21, 22, 23, 32, 0)]
     assert _multi_call(lib, good, m=-1) == -1
-    assert _multi_call(lib, good, m=9) == -1
+    assert _multi_call(lib, good, m=17) == -1
     assert _multi_call(lib, good, n_in=100) == -1
     assert _multi_call(lib, good, bits=0) == -1
     assert _multi_call(lib, good, bits=9) == -1

@@ -190,7 +190,7 @@ TINY = [(128, 16), (128, 32), (256, 48), (384, 272), (1024, 1040)]
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])
 def test_linear_small_shapes(torch_cuda, fn, K):
     for (n_in, n_out) in TINY:
-        for m in ((1, 2, 3, 4, 5, 8) if fn == "gemv" else (1, 7, 16, 33)):
+        for m in ((1, 2, 3, 4, 5, 8, 9, 13, 16) if fn == "gemv" else (1, 7, 16, 33)):
             log(f"{fn} K={K} n_in={n_in} n_out={n_out} m={m}")
             words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [7, K, n_in, n_out, m])
             ref = O.linear(x, words, sign, scale, K)
@@ -359,6 +359,28 @@ def test_workload_prefill_gemm(torch_cuda):
     ws = ex.Workspace(8192, 28672, 8, 2048)
     for mm in synth.prefill_gemm():
         check_workload(torch_cuda, mm, "gemm", ws)
+
+
+def test_medium_m_gemv_and_split_gemm(torch_cuda):
+    # batched decode / chunked prefill sizes: the GEMV up to 16 rows, the GEMM
+    # with its input dimension split across workgroups below ~256 blocks
+    import decode_gemm_exl3_amd as ex
+    ws = ex.Workspace(14336, 14336, 8, 256)
+    rng = np.random.default_rng(5)
+    for fn, n_in, n_out, K, m in [("gemv", 4096, 14336, 3, 12), ("gemv", 14336, 4096, 4, 16),
+                                  ("gemm", 4096, 14336, 3, 17), ("gemm", 14336, 4096, 2, 64),
+                                  ("gemm", 4096, 4096, 4, 256), ("gemm", 4096, 1024, 5, 100)]:
+        mm = synth.Matmul(f"{fn}_m{m}", n_in, n_out, K, m, [0, 7, n_in, n_out, m])
+        check_workload(torch_cuda, mm, fn, ws)
+
+
+def test_linear_dispatch(torch_cuda):
+    # the measured table: GEMV for small m * n_in, the split GEMM beyond
+    for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12)]:
+        log(f"linear n_in={n_in} n_out={n_out} K={K} m={m}")
+        words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [19, n_in, m])
+        y = run_linear(torch_cuda, "linear", words, x, sign, scale, K)
+        assert rel_fro(y, O.linear(x, words, sign, scale, K)) <= TOL
 
 
 def test_workload_stack_sampled_layers(torch_cuda):
