@@ -291,6 +291,42 @@ def llama70b_rates(torch, ex, replicas=3, steps=20):
     return out
 
 
+def medium_m(torch, ex, ms=(16, 32, 64, 128, 256), n_in=4096, n_out=14336, K=4, replicas=4):
+    """Batched decode and chunked prefill sizes through exl3_linear (the GEMV or
+    the split GEMM, as its table picks): us per call, weight GB/s and TFLOP/s."""
+    import synth
+    w = torch.from_numpy(synth.words_only(n_in, n_out, K, [0, 8, K]).view(np.int16)).cuda()
+    reps = [w] + [w.clone() for _ in range(replicas - 1)]
+    sign = torch.ones(n_in, dtype=torch.float16, device="cuda")
+    scale = torch.full((n_out,), 0.02, dtype=torch.float16, device="cuda")
+    ws = ex.Workspace(n_in, n_out, K, max(ms))
+    out = {}
+    for m in ms:
+        x = torch.randn((m, n_in), device="cuda").half()
+        y = torch.empty((m, n_out), dtype=torch.float16, device="cuda")
+        for i in range(2):
+            ex.linear(x, reps[i % replicas], sign, scale, K, workspace=ws, y=y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        st = torch.cuda.Stream()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(8):
+                ex.linear(x, reps[i % replicas], sign, scale, K, workspace=ws, y=y)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 40 * 1e3
+        out[f"m{m}"] = {"us": round(us, 1), "weight_gbs": round(n_in * n_out * K / 8 / us / 1e3, 1),
+                        "tflops": round(2.0 * m * n_in * n_out / us / 1e6, 1)}
+    return out
+
+
 def encode_rates(torch, ex, n_tiles=2048, Ks=(2, 3, 4)):
     """Tail-biting Viterbi encoder: tiles/s on unit-Gaussian tiles and the mean
     squared error per weight it reaches."""
@@ -394,6 +430,7 @@ def main():
                                             "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
         extra["llama70b_m1"] = llama70b_rates(torch, ex)
         extra["encode"] = encode_rates(torch, ex)
+        extra["medium_m_4096x14336_k4"] = medium_m(torch, ex)
         # the byte-sum (dp4a) codebook on the K=4 MLP launches and the GEMM
         calls = build_mlp(torch, ex, 1, Ks=(4,), replicas=args.replicas)
         for c in calls:
