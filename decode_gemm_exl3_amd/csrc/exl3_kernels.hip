@@ -39,46 +39,83 @@ __global__ __launch_bounds__(256) void decode_tile_kernel(const uint16_t* __rest
     }
 }
 
-// ---------------------------------------------------------------------------
-// 128-point Hadamard of one block held by one wave: lane l has elements l and
-// l + 64.  Butterfly stages in natural (Sylvester) order.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void fwht128_wave(float& v0, float& v1, int lane) {
-    float a = v0 + v1, d = v0 - v1;
-    v0 = a;
-    v1 = d;
-#pragma unroll
-    for (int h = 32; h >= 1; h >>= 1) {
-        const float u0 = __shfl_xor(v0, h, 64);
-        const float u1 = __shfl_xor(v1, h, 64);
-        const bool up = (lane & h) != 0;
-        v0 = up ? (u0 - v0) : (v0 + u0);
-        v1 = up ? (u1 - v1) : (v1 + u1);
-    }
-}
-
 // 128-point Hadamard of one block held by 16 lanes (one DPP row), 8 values per
-// lane: lane l16 holds elements 8*l16 + e, e = 0..7.  Stages on index bits 0..2
-// are in-lane; bits 3..6 are lane bits 0..3, exchanged with DPP: xor 1 and xor 2
-// by quad permutes, xor 4 as half-row mirror then quad xor 3, xor 8 as row
-// mirror then half-row mirror.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+// lane: lane l16 holds inputs 8*l16 + e, e = 0..7.  H128 = H16 (x) H8 on
+// (l16, e), so the three stages on e run inside the lane and the 16-point
+// transform across the lanes of the row.
+//
+// Across lanes, any four butterfly stages whose partner masks form a basis of
+// GF(2)^4 give the 16-point Walsh-Hadamard transform up to a permutation and
+// signs of the outputs.  The masks 15, 7, 1, 2 are each one DPP pattern (row
+// mirror, half-row mirror, two quad permutes).  Stage i pairs lane l with
+// l ^ m_i; with b_i a bit set in m_i (3, 2, 0, 1), the lane with bit b_i clear
+// keeps v + v', the other v' - v.  Keeping instead u = sigma * v per lane, with
+// sigma the product of the stages' signs so far, every stage becomes
+// u += c_i(l) * u(l ^ m_i) with c_i(l) = -1 exactly when bit b_i of l is set:
+// one v_fmac_f32 with a DPP source per value.  After the four stages lane l
+// holds, up to the sign s(l), outputs 8 * pos(l) + e, where
+// pos(l) = 5 l0 ^ 6 l1 ^ 12 l2 ^ 8 l3 (l0..l3 the bits of l) and s(l) = -1 for
+// the lanes of the mask 0xF9F6.  Both were derived by carrying the unit
+// vectors through the stages; the parity tests check the result against the
+// Hadamard matrix itself.
+struct RowFwht {
+    float c[4];  // +-1.0: the partner's factor in cross-lane stage i
+    float osc;   // s(l) / 128: the sign the stages leave, and the x'/128 scale
+    int pos;     // the 8-input group of the block this lane ends up holding
+};
+
+__device__ __forceinline__ RowFwht row_fwht_consts(int l16) {
+    RowFwht k;
+    k.c[0] = (l16 & 8) ? -1.0f : 1.0f;
+    k.c[1] = (l16 & 4) ? -1.0f : 1.0f;
+    k.c[2] = (l16 & 1) ? -1.0f : 1.0f;
+    k.c[3] = (l16 & 2) ? -1.0f : 1.0f;
+    k.osc = ((0xF9F6 >> l16) & 1) ? -1.0f / 128.0f : 1.0f / 128.0f;
+    k.pos = ((l16 & 1) ? 5 : 0) ^ ((l16 & 2) ? 6 : 0) ^ ((l16 & 4) ? 12 : 0) ^ ((l16 & 8) ? 8 : 0);
+    return k;
 }
 
-__device__ __forceinline__ float lane_xor(float v, int h) {
-    switch (h) {
-        case 1: return dpp_f<0xB1>(v);                     // quad_perm [1,0,3,2]
-        case 2: return dpp_f<0x4E>(v);                     // quad_perm [2,3,0,1]
-        case 4: return dpp_f<0x1B>(dpp_f<0x141>(v));       // half-row mirror, quad [3,2,1,0]
-        default: return dpp_f<0x141>(dpp_f<0x140>(v));     // row mirror, half-row mirror
+// u[e] += c * u[e] of the partner lane, for the 8 values.  v_fmac_f32 takes a
+// DPP source only in assembly (the compiler folds DPP into adds and multiplies,
+// not into the accumulating multiply-add).  The leading s_nop gives the wait
+// states a DPP read needs after a vector write of its source (2) or of EXEC
+// (5); within the block each value is read once, by the instruction that
+// rewrites it.
+#define EXL3_XLANE_STAGE(DPP)                                                                             \
+    asm volatile("s_nop 4\n"                                                                              \
+                 "v_fmac_f32_dpp %0, %0, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %1, %1, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %2, %2, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %3, %3, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %4, %4, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %5, %5, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %6, %6, %8 " DPP " row_mask:0xf bank_mask:0xf\n"                       \
+                 "v_fmac_f32_dpp %7, %7, %8 " DPP " row_mask:0xf bank_mask:0xf"                         \
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), \
+                   "+v"(v[7])                                                                             \
+                 : "v"(cc))
+
+// Sign flip and first stage straight from the packed fp16 input: x * sign is
+// exact in fp16 (sign is +-1), and the sum and difference of two fp16 values
+// are exact in fp32.
+__device__ __forceinline__ void row_load_pairs(const u32x4_t& xv, const u32x4_t& sv, float (&v)[8]) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        // (element copies first: a bit cast straight from a vector element reads element 0)
+        const uint32_t xw = xv[d], sw = sv[d];
+        const h2_t p = __builtin_bit_cast(h2_t, xw) * __builtin_bit_cast(h2_t, sw);
+        const float a = (float)p[0], b = (float)p[1];
+        v[2 * d] = a + b;
+        v[2 * d + 1] = a - b;
     }
 }
 
-__device__ __forceinline__ void fwht128_row(float (&v)[8], int l16) {
+// The remaining stages: in-lane on e bits 1 and 2, then the four cross-lane
+// stages.  Afterwards v[e] * k.osc = x'[8 * k.pos + e] / 128 of the block.
+__device__ __forceinline__ void fwht128_row(float (&v)[8], const RowFwht& k) {
 #pragma unroll
-    for (int h = 1; h < 8; h <<= 1)
+    for (int h = 2; h < 8; h <<= 1)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if ((e & h) == 0) {
@@ -86,42 +123,48 @@ __device__ __forceinline__ void fwht128_row(float (&v)[8], int l16) {
                 v[e] = a + b;
                 v[e + h] = a - b;
             }
-#pragma unroll
-    for (int h = 1; h < 16; h <<= 1) {
-        const bool up = (l16 & h) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float u = lane_xor(v[e], h);
-            v[e] = up ? (u - v[e]) : (v[e] + u);
-        }
-    }
+    float cc = k.c[0];
+    EXL3_XLANE_STAGE("row_mirror");
+    cc = k.c[1];
+    EXL3_XLANE_STAGE("row_half_mirror");
+    cc = k.c[2];
+    EXL3_XLANE_STAGE("quad_perm:[1,0,3,2]");
+    cc = k.c[3];
+    EXL3_XLANE_STAGE("quad_perm:[2,3,0,1]");
 }
+#undef EXL3_XLANE_STAGE
 
-// x'/128 rounded to fp16: exact power-of-two scaling keeps any fp16 input in range.
-__device__ __forceinline__ uint16_t rot_to_half(float v) {
-    return __half_as_ushort(__float2half_rn(v * (1.0f / 128.0f)));
+// fp16(x'/128) of two values, packed (RNE, one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_half2(float a, float b) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    const h2_t h = h2_t{(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, h);
 }
 
 // ---------------------------------------------------------------------------
-// rotate: xr[r][k] = fp16((H128 (sign * x[r]))[k] / 128), one wave per block.
+// rotate: xr[r][k] = fp16((H128 (sign * x[r]))[k] / 128).  16 lanes per block,
+// 8 inputs per lane (one 16-byte load and store), 16 blocks per workgroup.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ sign, int m, int n_in,
                                                      uint16_t* __restrict__ xr) {
-    const int lane = threadIdx.x & 63;
-    const int64_t blk = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int l16 = threadIdx.x & 15;
+    const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
     const int nblk_row = n_in >> 7;
+    // whole rows of 16 lanes leave together, so the DPP rows stay complete
     if (blk >= (int64_t)m * nblk_row) return;
     const int64_t row = blk / nblk_row;
-    const int col0 = (int)(blk % nblk_row) << 7;
-    const uint16_t* xp = x + row * n_in + col0;
-    float v0 = __half2float(__ushort_as_half(xp[lane])) * __half2float(__ushort_as_half(sign[col0 + lane]));
-    float v1 = __half2float(__ushort_as_half(xp[lane + 64])) *
-               __half2float(__ushort_as_half(sign[col0 + lane + 64]));
-    fwht128_wave(v0, v1, lane);
-    uint16_t* o = xr + row * n_in + col0;
-    o[lane] = rot_to_half(v0);
-    o[lane + 64] = rot_to_half(v1);
+    const int col = (int)(blk % nblk_row) * 128;
+    const RowFwht k = row_fwht_consts(l16);
+    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * n_in + col + l16 * 8);
+    const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(sign + col + l16 * 8);
+    float v[8];
+    row_load_pairs(xv, sv, v);
+    fwht128_row(v, k);
+    u32x4_t o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = pack_half2(v[2 * d] * k.osc, v[2 * d + 1] * k.osc);
+    *reinterpret_cast<u32x4_t*>(xr + row * n_in + col + k.pos * 8) = o;
 }
 
 // ---------------------------------------------------------------------------
@@ -217,6 +260,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
 
     const bool adata = n < M;
     const CbRegs cr = cb_regs<CB>();
+    const RowFwht fk = row_fwht_consts(lane & 15);
     int q = 0;
     for (int c = 0; c < p.n_kchunks; ++c) {
         const int tc0 = c * p.kc;
@@ -228,28 +272,21 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         {
             // 16 lanes per 128-input block, 8 inputs per lane (one 16-byte load)
             const int nblk = (kcount * 16) >> 7;
-            const int l16 = lane & 15;
             for (int blk = tid >> 4; blk < M * nblk; blk += 4 * W) {
                 const int r = blk / nblk, bb = blk % nblk;
-                const int col = tc0 * 16 + bb * 128 + l16 * 8;
+                const int col = tc0 * 16 + bb * 128 + (lane & 15) * 8;
                 const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)r * p.n_in + col);
                 const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(p.sign + col);
                 float v[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t xw = xv[e >> 1], sw = sv[e >> 1];
-                    const int sh = (e & 1) * 16;
-                    v[e] = __half2float(__ushort_as_half((unsigned short)(xw >> sh))) *
-                           __half2float(__ushort_as_half((unsigned short)(sw >> sh)));
-                }
-                fwht128_row(v, l16);
+                row_load_pairs(xv, sv, v);
+                fwht128_row(v, fk);
                 uint32_t d[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t h = rot_to_half(v[e]);
-                    d[e] = h | (h << 16);
+                    const float t = v[e] * fk.osc;
+                    d[e] = pack_half2(t, t);  // duplicated for the two codebook halves
                 }
-                u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + bb * 128 + l16 * 8);
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + bb * 128 + fk.pos * 8);
                 dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
                 dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
             }
