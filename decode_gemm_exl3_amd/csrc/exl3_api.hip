@@ -62,50 +62,76 @@ int64_t ws_total(int n_in, int n_out, int max_m) {
     return best;
 }
 
-// GEMV launch plan.  Persistent workgroups (about one per CU) own strips
-// round-robin.  The input dimension is cut into as few chunks as the LDS budget
-// allows (x' of a chunk lives in LDS).  Within a strip, W waves share the steps
-// (4 tile columns each); W, the steps per wave (nsw) and the steps in flight
-// (pf, nsw % pf == 0) are picked to waste few padded steps while keeping many
-// loads in flight.
+// GEMV launch plan.  Persistent workgroups own strips round-robin.  The input
+// dimension is cut into as few chunks as the LDS budget allows (x' of a chunk
+// lives in LDS).  Within a strip, W waves share the steps (4 tile columns
+// each); nsw steps per wave, pf of them in flight (nsw % pf == 0).
+//
+// The shape of the launch comes from a sweep on MI355X over workgroups per CU
+// (1, 2), W (4 .. 16) and pf (2, 4, 8) on the Llama 8B and 70B projections at
+// m = 1 and K = 2, 4:
+//   - two workgroups of 8 waves per CU beat one of 16 by 5-10 % wherever the
+//     strips give each workgroup at least one and both fit in LDS (one
+//     workgroup's rotation and final sums overlap the other's stream);
+//   - with one workgroup per CU, 16 waves win once a workgroup walks 512 or
+//     more steps, 8 waves below that;
+//   - pf = 4 is best or within noise of it everywhere (pf = 2 starves the
+//     loads, pf = 8 pads short strips).
+// Other shapes (m > 1 with long inputs, chunked inputs) fall back to the
+// search that wastes the fewest padded steps.
+bool plan_chunks(exl3::GemvParams* p, int grid, int nk, int w, int pf, size_t lds_cap) {
+    int kc = (p->tiles_in + nk - 1) / nk;
+    kc = (kc + 7) & ~7;
+    const int steps = (kc + 3) / 4;
+    int nsw = (steps + w - 1) / w;
+    nsw = (nsw + pf - 1) / pf * pf;
+    const int nj = (p->n_strips + grid - 1) / grid;
+    if (exl3::gemv_lds_bytes(p->m, w, nsw, pf, nj) > lds_cap) return false;
+    p->kc = kc;
+    p->n_kchunks = (p->tiles_in + kc - 1) / kc;
+    p->waves = w;
+    p->nsw = nsw;
+    p->pf = pf;
+    p->grid = grid;
+    return true;
+}
+
 bool plan_gemv(exl3::GemvParams* p) {
     static const int nk_force = env_int("EXL3_GEMV_KCHUNKS", 0);
-    static const int grid_mul = env_int("EXL3_GEMV_GRID_PER_CU", 1);
-    int grid = cu_count() * grid_mul;
+    static const int grid_force = env_int("EXL3_GEMV_GRID_PER_CU", 0);
+    static const int pf_force = env_int("EXL3_GEMV_PF", 0);
+    static const int w_force = env_int("EXL3_GEMV_WAVES", 0);
+    const int cus = cu_count();
+    const size_t budget = (size_t)exl3::GEMV_LDS_BUDGET;
+    if (nk_force == 0 && grid_force == 0 && pf_force == 0 && w_force == 0) {
+        if (p->n_strips >= 2 * cus && plan_chunks(p, 2 * cus, 1, 8, 4, budget / 2)) return true;
+        const int grid = p->n_strips < cus ? p->n_strips : cus;
+        const int64_t wg_steps = (int64_t)((p->n_strips + grid - 1) / grid) * ((p->tiles_in + 3) / 4);
+        if (plan_chunks(p, grid, 1, wg_steps >= 512 ? 16 : 8, 4, budget)) return true;
+    }
+    int grid = cus * (grid_force > 0 ? grid_force : 1);
     if (grid > p->n_strips) grid = p->n_strips;
     const int nj = (p->n_strips + grid - 1) / grid;
     for (int nk = nk_force > 0 ? nk_force : 1; nk <= p->tiles_in / 8; ++nk) {
         int kc = (p->tiles_in + nk - 1) / nk;
         kc = (kc + 7) & ~7;
-        const int n_kchunks = (p->tiles_in + kc - 1) / kc;
         const int steps = (kc + 3) / 4;
         double best = 1e30;
-        int bw = 0, bn = 0, bp = 0;
-        static const int pf_force = env_int("EXL3_GEMV_PF", 0);
-        static const int w_force = env_int("EXL3_GEMV_WAVES", 0);
-        for (int pf : {8, 4, 2}) {
+        int bw = 0, bp = 0;
+        for (int pf : {4, 8, 2}) {
             if (pf_force > 0 && pf != pf_force) continue;
             for (int w = 16; w >= 4; --w) {
                 if (w_force > 0 && w != w_force) continue;
                 int nsw = (steps + w - 1) / w;
                 nsw = (nsw + pf - 1) / pf * pf;
-                const double penalty = pf == 8 ? 1.0 : (pf == 4 ? 1.06 : 1.2);
+                const double penalty = pf == 4 ? 1.0 : (pf == 8 ? 1.03 : 1.2);
                 const double cost = (double)w * nsw * penalty + 0.01 * (16 - w);
-                if (exl3::gemv_lds_bytes(p->m, w, nsw, pf, nj) > (size_t)exl3::GEMV_LDS_BUDGET) continue;
-                if (cost < best) { best = cost; bw = w; bn = nsw; bp = pf; }
+                if (exl3::gemv_lds_bytes(p->m, w, nsw, pf, nj) > budget) continue;
+                if (cost < best) { best = cost; bw = w; bp = pf; }
             }
         }
-        if (bw == 0) {
-            if (nk_force > 0) return false;
-            continue;
-        }
-        p->kc = kc;
-        p->n_kchunks = n_kchunks;
-        p->waves = bw;
-        p->nsw = bn;
-        p->pf = bp;
-        p->grid = grid;
-        return true;
+        if (bw > 0 && plan_chunks(p, grid, nk, bw, bp, budget)) return true;
+        if (nk_force > 0) return false;
     }
     return false;
 }
