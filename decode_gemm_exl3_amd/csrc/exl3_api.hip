@@ -31,6 +31,9 @@ int cu_count() {
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Input length from which a GEMV of 2..8 rows with enough workspace rotates its input in a pre-pass.
+constexpr int GEMV_PREROT_MIN_N_IN = 12288;
+
 // Workspace needs.  Nothing in the workspace survives between calls, so each
 // call lays out only what it uses from offset 0:
 //   gemv: nothing (one kernel, partial sums stay in LDS);
@@ -136,6 +139,19 @@ bool plan_gemv(exl3::GemvParams* p) {
     return false;
 }
 
+// Whether a GEMV rotates its input once in a pre-pass (into the workspace)
+// rather than in every workgroup.  Each workgroup's rotation costs vector
+// issue in proportion to m * n_in; the pre-pass costs one more launch and a
+// copy of the rotated rows from L2 into every workgroup's LDS.  Measured on
+// MI355X (8B and 70B projections, m = 1..16): the pre-pass wins 4-8 % for long
+// inputs (n_in >= 12288) at 2 <= m <= 8, loses up to 2 us at m = 1 (the extra
+// launch) and loses at m = 16 on long inputs (the copies of many LDS chunks).
+bool gemv_prerotate(int m, int n_in) {
+    static const int force = env_int("EXL3_GEMV_PREROT", -1);
+    if (force >= 0) return force > 0;
+    return m >= 2 && m <= 8 && n_in >= GEMV_PREROT_MIN_N_IN;
+}
+
 // The bits argument: K in the low byte, the codebook flag above it.
 int k_of(int32_t bits) { return bits & 0xFF; }
 int cb_of(int32_t bits) { return (bits & EXL3_CODEBOOK_BYTE_SUM) ? 1 : 0; }
@@ -192,8 +208,6 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles, uint1
 int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t n_in, int32_t bits,
                     const exl3_proj_t* proj, int32_t n_proj, void* workspace, size_t workspace_bytes,
                     void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (m < 0 || m > EXL3_GEMV_MAX_M || bad_bits(bits) || n_in <= 0 || (n_in % 128) != 0) return EXL3_EINVAL;
     if (!proj || n_proj < 1 || n_proj > EXL3_GEMV_MAX_PROJ) return EXL3_EINVAL;
     for (int i = 0; i < n_proj; ++i) {
@@ -232,8 +246,15 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
     p.n_in = n_in;
     p.tiles_in = n_in / 16;
     p.n_strips = (int)strips;
+    p.xr = nullptr;
     if (!plan_gemv(&p)) return EXL3_EUNSUPPORTED;
-    hipError_t e = exl3::launch_gemv(k_of(bits), cb_of(bits), p, (hipStream_t)stream);
+    hipStream_t s = (hipStream_t)stream;
+    if (gemv_prerotate(m, n_in) && workspace && (int64_t)workspace_bytes >= gemm_rot_bytes(n_in, m)) {
+        uint16_t* xr = static_cast<uint16_t*>(workspace);
+        if (exl3::launch_rotate(x, sign, m, n_in, xr, s) != hipSuccess) return EXL3_EHIP;
+        p.xr = xr;
+    }
+    hipError_t e = exl3::launch_gemv(k_of(bits), cb_of(bits), p, s);
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
 }
 

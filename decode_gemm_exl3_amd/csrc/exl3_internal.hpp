@@ -16,6 +16,7 @@ constexpr int GEMV_MAX_PROJ = 4;  // projections sharing one input in one GEMV l
 struct GemvParams {
     const uint16_t* x;
     const uint16_t* sign;
+    const uint16_t* xr;  // x'/128 in fp16 [m][n_in] from the rotation pre-pass, or null: rotate in the kernel
     const uint16_t* trellis[GEMV_MAX_PROJ];
     const uint16_t* out_scale[GEMV_MAX_PROJ];
     uint16_t* y[GEMV_MAX_PROJ];
@@ -33,8 +34,9 @@ struct GemvParams {
 };
 
 // LDS of a GEMV workgroup: x' rows, a zero block, per-wave partial sums of its nj strips.
+constexpr int GEMV_ROW_PAD = 4;  // dwords after each LDS row of x' (bank spread)
 __host__ __device__ inline size_t gemv_lds_bytes(int m, int waves, int nsw, int pf, int nj) {
-    return ((size_t)m * waves * nsw * 64 + (size_t)pf * 64 + (size_t)nj * waves * m * 16) * 4;
+    return ((size_t)m * ((size_t)waves * nsw * 64 + GEMV_ROW_PAD) + (size_t)pf * 64 + (size_t)nj * waves * m * 16) * 4;
 }
 
 struct GemmParams {

@@ -208,7 +208,10 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     const int M = p.m;
     const int W = p.waves;
     const int nsw = p.nsw;                 // steps per wave per (strip, chunk), a multiple of PF
-    const int xcols = W * nsw * 64;        // dwords per LDS row
+    // dwords per LDS row: the x' columns plus 4, so that the rows the 16 lanes
+    // of a fragment read start 16 bytes apart in the banks (an unpadded stride
+    // is a multiple of 256 bytes and puts all 16 rows on the same banks)
+    const int xcols = W * nsw * 64 + GEMV_ROW_PAD;
     const int G = gridDim.x;
     const int b = blockIdx.x;
     const int nj = (p.n_strips - b + G - 1) / G;   // strips of this workgroup
@@ -269,7 +272,25 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         if (c > 0) __syncthreads();  // every wave is done with the previous chunk
         for (int i = kcount * 16 + tid; i < xcols; i += 64 * W)
             for (int r = 0; r < M; ++r) xs[r * xcols + i] = 0u;
-        {
+        if (p.xr) {
+            // rotated once by the pre-pass: copy the chunk, 8 inputs per lane,
+            // each duplicated for the two codebook halves
+            const int per_row = kcount * 2;  // 16-byte groups of a row in this chunk
+            for (int r = 0; r < M; ++r)
+                for (int c8 = tid; c8 < per_row; c8 += 64 * W) {
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p.xr + (int64_t)r * p.n_in + tc0 * 16 + c8 * 8);
+                    uint32_t d[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w2 = v[e];
+                        d[2 * e] = (w2 & 0xFFFFu) | (w2 << 16);
+                        d[2 * e + 1] = (w2 >> 16) | (w2 & 0xFFFF0000u);
+                    }
+                    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + c8 * 8);
+                    dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
+                    dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+                }
+        } else {
             // 16 lanes per 128-input block, 8 inputs per lane (one 16-byte load)
             const int nblk = (kcount * 16) >> 7;
             for (int blk = tid >> 4; blk < M * nblk; blk += 4 * W) {

@@ -107,9 +107,14 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
  *   sign      : fp16 [n_in], entries +-1
  *   out_scale : fp16 [n_out]
  *   y         : fp16 [m][n_out] (overwritten; fp32 accumulation, round to nearest even)
- *   workspace : device scratch of at least exl3_pack_info(...).workspace_bytes
- *               bytes for max_m >= m.  Its contents need no initialisation and
- *               are meaningless after the call.  Calls that may run at the same
+ *   workspace : optional device scratch (NULL and 0 are accepted).  With at
+ *               least m*n_in*2 bytes (rounded up to 256; the size
+ *               exl3_pack_info gives for max_m >= m always suffices) an input
+ *               of 2..8 rows and n_in >= 12288 is rotated once by a pre-pass
+ *               into it; otherwise every workgroup rotates the input itself.
+ *               Both give the same y bit for bit.  Its contents need no
+ *               initialisation and are meaningless after the call; it must not
+ *               overlap x, y or the weights.  Calls that may run at the same
  *               time (different streams) need separate workspaces.
  * m == 0 is a no-op.  m > EXL3_GEMV_MAX_M or m < 0 gives EXL3_EINVAL (use exl3_gemm).
  */
@@ -139,7 +144,7 @@ typedef struct exl3_proj_t {
  *                            same input sign vector (one rotated input).
  *   proj[0..n_proj-1]      : per projection trellis, out_scale, y and n_out.
  *                            The y buffers must not overlap each other or x.
- *   workspace              : as exl3_gemv (the GEMV needs none today).
+ *   workspace              : as exl3_gemv (optional; used for the rotation pre-pass).
  * Each proj[i].y equals what exl3_gemv gives for that projection, up to fp32
  * summation order.  m == 0 is a no-op.  EXL3_EINVAL for m outside 0..EXL3_GEMV_MAX_M, n_proj
  * outside 1..EXL3_GEMV_MAX_PROJ, a null pointer, a bad shape or two identical y.

@@ -214,6 +214,25 @@ def test_gemv_split_and_ragged(torch_cuda):
             assert rel_fro(y, ref) <= TOL, (n_in, n_out, K, m, rep)
 
 
+def test_gemv_rotation_pre_pass_and_in_kernel(torch_cuda):
+    # with a workspace a long input of 2..8 rows is rotated once by a pre-pass;
+    # without one every workgroup rotates it: both against the oracle, on
+    # chunked and unchunked inputs, and the two results against each other
+    import decode_gemm_exl3_amd as ex
+    torch = torch_cuda
+    for (n_in, n_out, K, m) in [(14336, 272, 3, 8), (28672, 64, 2, 2), (12288, 4112, 5, 5), (4096, 528, 4, 16)]:
+        log(f"gemv rotation paths n_in={n_in} n_out={n_out} K={K} m={m}")
+        words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [21, n_in, n_out, K, m])
+        ref = O.linear(x, words, sign, scale, K)
+        y_pre = run_linear(torch, "gemv", words, x, sign, scale, K, ws=ex.Workspace(n_in, n_out, K, m))
+        y_in = ex.gemv_multi(to_dev(torch, x), [(to_dev(torch, words), to_dev(torch, scale))], to_dev(torch, sign), K)[0]
+        torch.cuda.synchronize()
+        y_in = y_in.cpu().numpy()
+        assert rel_fro(y_pre, ref) <= TOL and rel_fro(y_in, ref) <= TOL, (n_in, n_out, K, m)
+        # the same rotation arithmetic in both places: the same bits
+        assert np.array_equal(y_pre.view(np.uint16), y_in.view(np.uint16)), (n_in, n_out, K, m)
+
+
 def test_workspace_reuse_across_shapes_and_m(torch_cuda):
     import decode_gemm_exl3_amd as ex
     ws = ex.Workspace(4096, 4096, 8, 64)
