@@ -143,28 +143,29 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
 
 // ---------------------------------------------------------------------------
 // rotate: xr[r][k] = fp16((H128 (sign * x[r]))[k] / 128).  16 lanes per block,
-// 8 inputs per lane (one 16-byte load and store), 16 blocks per workgroup.
+// 8 inputs per lane (one 16-byte load and store); a workgroup covers 16
+// blocks of a row (blockIdx.x) and walks rows blockIdx.y, + gridDim.y, ...
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ sign, int m, int n_in,
                                                      uint16_t* __restrict__ xr) {
     const int l16 = threadIdx.x & 15;
-    const int64_t blk = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-    const int nblk_row = n_in >> 7;
+    const int bb = blockIdx.x * 16 + (threadIdx.x >> 4);  // 128-input block within the row
     // whole rows of 16 lanes leave together, so the DPP rows stay complete
-    if (blk >= (int64_t)m * nblk_row) return;
-    const int64_t row = blk / nblk_row;
-    const int col = (int)(blk % nblk_row) * 128;
+    if (bb >= (n_in >> 7)) return;
+    const int col = bb * 128 + l16 * 8;
     const RowFwht k = row_fwht_consts(l16);
-    const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + row * n_in + col + l16 * 8);
-    const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(sign + col + l16 * 8);
-    float v[8];
-    row_load_pairs(xv, sv, v);
-    fwht128_row(v, k);
-    u32x4_t o;
+    const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(sign + col);
+    for (int row = blockIdx.y; row < m; row += gridDim.y) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + (int64_t)row * n_in + col);
+        float v[8];
+        row_load_pairs(xv, sv, v);
+        fwht128_row(v, k);
+        u32x4_t o;
 #pragma unroll
-    for (int d = 0; d < 4; ++d) o[d] = pack_half2(v[2 * d] * k.osc, v[2 * d + 1] * k.osc);
-    *reinterpret_cast<u32x4_t*>(xr + row * n_in + col + k.pos * 8) = o;
+        for (int d = 0; d < 4; ++d) o[d] = pack_half2(v[2 * d] * k.osc, v[2 * d + 1] * k.osc);
+        *reinterpret_cast<u32x4_t*>(xr + (int64_t)row * n_in + bb * 128 + k.pos * 8) = o;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -406,8 +407,9 @@ hipError_t launch_decode(int K, int cb, const uint16_t* words, int64_t n_tiles, 
 }
 
 hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr, hipStream_t s) {
-    const int64_t blocks = ((int64_t)m * (n_in >> 7) + 3) / 4;
-    hipLaunchKernelGGL(rotate_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, sign, m, n_in, xr);
+    const unsigned gx = (unsigned)(((n_in >> 7) + 15) / 16);
+    const unsigned gy = (unsigned)(m < 65535 ? m : 65535);
+    hipLaunchKernelGGL(rotate_kernel, dim3(gx, gy), dim3(256), 0, s, x, sign, m, n_in, xr);
     return hipGetLastError();
 }
 
