@@ -1,5 +1,6 @@
 // exl3_kernels.hip - decode, input rotation and GEMV kernels for gfx950.
 #include <atomic>
+#include <type_traits>
 
 #include "exl3_device.hpp"
 #include "exl3_internal.hpp"
@@ -216,7 +217,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     const int G = gridDim.x;
     const int b = blockIdx.x;
     const int nj = (p.n_strips - b + G - 1) / G;   // strips of this workgroup
-    const int nseg = nj * p.n_kchunks;             // (chunk, strip) segments, chunk-major
 
     uint32_t* zero = xs + M * xcols;
     float* red = reinterpret_cast<float*>(zero + PF * 64);
@@ -233,18 +233,19 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         return (s >= p.strip_end[0]) + (s >= p.strip_end[1]) + (s >= p.strip_end[2]);
     };
     auto proj_begin = [&](int pi) -> int { return pi == 0 ? 0 : p.strip_end[pi - 1]; };
-    // segment q = (chunk q / nj, strip b + (q % nj) * G): its projection's
-    // resource, the byte offset of its step 0 and the offset of the
-    // projection's last step.  Step offsets are clamped to that last step, so a
-    // wave's padding steps past the end of the last strip re-read real weights
-    // (they meet zero inputs) instead of leaving the buffer.
+    // segment (c, j) = (chunk c, strip b + j * G), taken in the order (0, 0),
+    // (0, 1), .., (1, 0), ..: its projection's resource, the byte offset of its
+    // step 0 and the offset of the projection's last step.  Step offsets are
+    // clamped to that last step, so a wave's padding steps past the end of the
+    // last strip re-read real weights (they meet zero inputs) instead of
+    // leaving the buffer.
     struct Seg {
         __amdgpu_buffer_rsrc_t rs;
         uint32_t off, lim;
     };
-    auto seg_at = [&](int q) -> Seg {
-        if (q >= nseg) return Seg{make_rsrc(p.trellis[0], 0), 0u, 0u};  // past the end: an empty buffer reads zeros
-        const int c = q / nj, s = b + (q % nj) * G;
+    auto seg_at = [&](int c, int j) -> Seg {
+        if (c >= p.n_kchunks) return Seg{make_rsrc(p.trellis[0], 0), 0u, 0u};  // past the end: an empty buffer reads zeros
+        const int s = b + j * G;
         const int pi = proj_of(s);
         const int ls = s - proj_begin(pi);
         const int64_t bytes = (int64_t)(p.n_out[pi] >> 4) * p.tiles_in * TILE_B;
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     // ---- weight stream first --------------------------------------------------
     uint32_t buf[PF][RowGeom<K>::NB];
     {
-        const Seg s0 = seg_at(0);
+        const Seg s0 = seg_at(0, 0);
 #pragma unroll
         for (int u = 0; u < PF; ++u) load_row<K>(s0.rs, loff, min(s0.off + u * STEP_B, s0.lim), buf[u]);
     }
@@ -265,7 +266,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     const bool adata = n < M;
     const CbRegs cr = cb_regs<CB>();
     const RowFwht fk = row_fwht_consts(lane & 15);
-    int q = 0;
     for (int c = 0; c < p.n_kchunks; ++c) {
         const int tc0 = c * p.kc;
         const int kcount = min(p.kc, p.tiles_in - tc0);
@@ -315,16 +315,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         }
         __syncthreads();
 
-        for (int j = 0; j < nj; ++j, ++q) {
+        Seg cur = seg_at(c, 0);
+        for (int j = 0; j < nj; ++j) {
             // this segment's x' fragments: data lanes walk their row, others read zeros
             const uint32_t* ap = adata ? xs + n * xcols + wave * nsw * 64 + g * 16 : zero;
             const int astep = adata ? PF * 64 : 0;
-            const Seg cur = seg_at(q), nxt = seg_at(q + 1);
-            // one accumulator per MFMA of a step: no back-to-back dependent MFMAs
-            f32x4_t acc[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            for (int st = 0; st < nsw; st += PF) {
+            const Seg nxt = j + 1 < nj ? seg_at(c, j + 1) : seg_at(c + 1, 0);
+            f32x4_t acc[4];  // one accumulator per MFMA of a step: no back-to-back dependent MFMAs
+            // one round of PF steps; the first round of a segment starts the
+            // accumulators from zero inside its first MFMAs
+            auto round = [&](int st, auto first) {
                 // refills of this round target the next round: same segment or the next
                 const bool same = st + PF < nsw;
                 const uint32_t roff = same ? cur.off + (st + PF) * STEP_B : nxt.off;
@@ -349,18 +349,22 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const u32x4_t bv = u32x4_t{qq[4 * t], qq[4 * t + 1], qq[4 * t + 2], qq[4 * t + 3]};
+                        const f32x4_t cin = (decltype(first)::value && u == 0) ? f32x4_t{0.f, 0.f, 0.f, 0.f} : acc[t];
                         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av[t]),
-                                                                         __builtin_bit_cast(half8_t, bv), acc[t], 0, 0, 0);
+                                                                         __builtin_bit_cast(half8_t, bv), cin, 0, 0, 0);
                     }
                 }
                 ap += astep;
-            }
+            };
+            round(0, std::true_type{});
+            for (int st = PF; st < nsw; st += PF) round(st, std::false_type{});
             // this wave's partial for strip j (its own slots: no barrier needed)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
                 if (r < M) red[((j * W + wave) * M + r) * 16 + n] += (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
             }
+            cur = nxt;
         }
     }
 
