@@ -136,10 +136,11 @@ def per_kernel_events(torch, ex, calls, replicas, steps):
     launches of that shape (weight replicas rotating), divided by `steps`."""
     stream = torch.cuda.current_stream()
     ev = []
-    # a long GPU sleep first, so that every launch below is queued before the
-    # GPU reaches it and the events time the GPU, not the host's launch rate
-    torch.cuda._sleep(int(5e7))
     for c in calls:
+        # a long GPU sleep before each batch, so that all its launches are
+        # queued before the GPU reaches them and the events time the GPU, not
+        # the host's launch rate
+        torch.cuda._sleep(int(5e7))
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(stream)
