@@ -43,7 +43,10 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
     constexpr int U = 1 << (16 - K);   // block minima per step
     constexpr int LOW = U - 1;         // overlap mask
     constexpr int BLK = 1 << K;        // states per block
-    __shared__ float M[U];
+    // block minima, double-buffered where LDS allows (step i writes buffer
+    // i & 1, so a step needs one barrier); K = 1 has one buffer and two barriers
+    constexpr int NMB = K >= 2 ? 2 : 1;
+    __shared__ float Mbuf[NMB][U];
     __shared__ float wt[256];
     __shared__ uint16_t path[256];
     __shared__ float red_c[ENC_THREADS / 64];
@@ -58,14 +61,24 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
     // Codebook values of the thread's states, recomputed where they are used:
     // registers hold the 128 costs, and a stored copy of the values (or fp32
     // conversions the compiler would hoist out of the step loop) would spill.
-    // The state base passes through an empty asm statement each step so that
-    // the compiler cannot hoist the recomputation.
+    // The product of state s + 1 is that of state s plus A (every state is
+    // below 2^16, so the products agree mod 2^32 with the multiply): walking a
+    // thread's states costs one add each.  The base passes through an empty
+    // asm statement each step so that the compiler cannot hoist the
+    // recomputation.
     const CbRegs cr = cb_regs<CB>();
-    int sb = s0;
-    auto value = [&](int k) -> float {
-        return __half2float(__ushort_as_half(cb_value<CB>(cb_lo<CB>((uint32_t)(sb + k), cr))));
+    constexpr uint32_t CA = CB == 0 ? CB_A : CB1_A;
+    uint32_t pb = (uint32_t)s0 * CA + (CB == 0 ? CB_B : CB1_B);
+    auto launder = [&]() { asm volatile("" : "+v"(pb)); };
+    // (w - c(state)) in fp32 from the product of the state: the codebook's
+    // fp16 value enters a v_fma_mix_f32 as -h * 1.0 + w, one rounding of the
+    // exact difference, the same result as converting h and subtracting
+    auto diff = [&](float w, uint32_t pk) -> float {
+        const uint32_t h = cb_value<CB>(cb_word<CB>(pk, cr));
+        float d;
+        asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(h), "v"(w));
+        return d;
     };
-    auto launder = [&]() { asm volatile("" : "+v"(sb)); };
     const __amdgpu_buffer_rsrc_t rback = make_rsrc(back, p.slot_bytes);
 
     float cost[ENC_STATES];
@@ -74,9 +87,10 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
     auto run_pass = [&](int rot, int v) -> int {
         {
             const float w0 = wt[rot & 255];
+            uint32_t pk = pb;
 #pragma unroll
-            for (int k = 0; k < ENC_STATES; ++k) {
-                const float d = w0 - value(k);
+            for (int k = 0; k < ENC_STATES; ++k, pk += CA) {
+                const float d = diff(w0, pk);
                 const float e = d * d;
                 cost[k] = (v < 0 || ((s0 + k) & LOW) == v) ? e : INFINITY;
                 if ((k & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bounded live values
@@ -84,6 +98,7 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
         }
         for (int i = 1; i < 256; ++i) {
             launder();
+            float* M = Mbuf[i % NMB];
             // ---- block minima of the previous costs (first minimum on ties)
             if constexpr (K <= 7) {
                 // the thread's NBLK blocks are consecutive u: their choices are
@@ -102,7 +117,8 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
                     M[(s0 >> K) + b] = best;
                     pk[b >> 2] |= (uint32_t)bj << (8 * (b & 3));
                     // one block at a time: interleaving the independent chains
-                    // would hold one comparison mask per element
+                    // would hold one comparison mask per element (a tree of
+                    // minima and a scan for the first index measured slower)
                     if ((b & 1) == 1 || BLK >= 16) __builtin_amdgcn_sched_barrier(0);
                 }
                 const uint32_t off = (uint32_t)(i * U + (s0 >> K));
@@ -151,20 +167,21 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
             // ---- new costs: M of each state's predecessor block plus its error
             const float wi = wt[(i + rot) & 255];
             const int u0 = s0 & LOW;  // the thread's 128 states map to u0 .. u0 + 127
+            uint32_t pk = pb;
 #pragma unroll
             for (int k = 0; k < ENC_STATES; k += 4) {
                 const float4 m4 = *reinterpret_cast<const float4*>(&M[u0 + k]);
                 const float mk[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float d = wi - value(k + e);
+                for (int e = 0; e < 4; ++e, pk += CA) {
+                    const float d = diff(wi, pk);
                     cost[k + e] = mk[e] + d * d;
                 }
                 // four states at a time: the scheduler may not compute all 64
                 // codebook values ahead of their use
                 __builtin_amdgcn_sched_barrier(0);
             }
-            __syncthreads();
+            if constexpr (NMB == 1) __syncthreads();  // M is rewritten by the next step
         }
         // ---- end state: the lowest-cost state (lowest index on ties), among
         // the states whose top 16-K bits are v for the constrained pass
