@@ -20,8 +20,9 @@
 // position 0); a second pass starts in the states with those low bits and ends
 // in the states whose top 16-K bits equal them, which makes the stream cyclic.
 //
-// Layout: 512 threads per tile (two waves per SIMD, so 256 registers each);
-// thread t owns the 128 consecutive states 128t..128t+127 and their costs in
+// Layout: 1024 threads per tile (four waves per SIMD, 128 registers each,
+// which hides the LDS and barrier latency better than two waves of 256);
+// thread t owns the 64 consecutive states 64t..64t+63 and their costs in
 // registers (the codebook values are recomputed each step).  M (2^(16-K)
 // floats) is exchanged through LDS.  The choice j of every
 // (step, u) goes to the caller's workspace (one slot of 256 * 2^(16-K) bytes
@@ -35,8 +36,8 @@
 
 namespace exl3 {
 
-constexpr int ENC_THREADS = 512;
-constexpr int ENC_STATES = 128;  // per thread
+constexpr int ENC_THREADS = 1024;
+constexpr int ENC_STATES = 64;  // per thread
 
 template <int K, int CB>
 __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
             launder();
             float* M = Mbuf[i % NMB];
             // ---- block minima of the previous costs (first minimum on ties)
-            if constexpr (K <= 7) {
+            if constexpr (BLK <= ENC_STATES) {
                 // the thread's NBLK blocks are consecutive u: their choices are
                 // NBLK consecutive bytes, stored at once
                 constexpr int NBLK = ENC_STATES / BLK;
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
                     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)pk[0], rback, off, 0u, 0);
                 }
             } else {
-                // a block spans 2^(K-7) neighbouring lanes
+                // a block spans 2^K / 64 neighbouring lanes
                 float best = cost[0];
                 int bj = 0;
 #pragma unroll
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
             __syncthreads();
             // ---- new costs: M of each state's predecessor block plus its error
             const float wi = wt[(i + rot) & 255];
-            const int u0 = s0 & LOW;  // the thread's 128 states map to u0 .. u0 + 127
+            const int u0 = s0 & LOW;  // the thread's 64 states map to u0 .. u0 + 63
             uint32_t pk = pb;
 #pragma unroll
             for (int k = 0; k < ENC_STATES; k += 4) {
