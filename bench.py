@@ -249,6 +249,40 @@ def recorded_traffic():
     return rec.get("hbm_bytes_per_launch")
 
 
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (one 32-bit lane-operation per lane and clock; a wave64 instruction takes
+# four clocks of a SIMD).
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def alu_roofline(ms_per_launch):
+    """The same launch against the vector-ALU issue peak: the decode makes the
+    GEMV issue-bound at K <= 4, so this is the roofline that binds."""
+    n = recorded_valu_insts()
+    if n is None:
+        return None
+    achieved = n * 64 / (ms_per_launch * 1e-3)
+    return {"bound": "alu", "kernel": "gemv_kernel<K=4> gate+up 4096->2x14336",
+            "achieved": round(achieved / 1e12, 2), "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
+            "unit": "T lane-ops/s", "frac": round(achieved / VALU_PEAK_LANE_OPS, 4),
+            "valu_insts_per_launch": int(n)}
+
+
+def recorded_valu_insts():
+    """Vector-ALU instructions (MFMAs excluded) per launch of the dominant
+    kernel from the committed counter profile, or None when the kernel
+    sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "gemv_gate_up_k4_llama8b_issue.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_hash") != kernel_sources_hash():
+        return None
+    return rec.get("valu_insts_without_mfma")
+
+
 def stack_tokens_per_s(torch, ex, fused=True, reps=20):
     """32-layer Llama-3.1-8B-shaped stack at m=1: tokens/s = 1 / (one graph
     replay of every projection of every layer, in model order, on one stream).
@@ -458,6 +492,7 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic()},
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "alu_roofline": alu_roofline(dom_ms),
         "extra": extra,
     }
     if not args.no_cpu:
