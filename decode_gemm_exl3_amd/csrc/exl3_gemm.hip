@@ -1,9 +1,10 @@
 // exl3_gemm.hip - decode-matmul for larger m on the matrix cores (gfx950).
 //
 // The input is rotated once by a pre-pass (x'/128 in fp16, workspace).  A
-// workgroup (8 waves, one per CU) owns a BM x BN = 256 x 256 block of y; wave w
-// owns rows 128 (w >> 2) .. +127 and outputs 64 (w & 3) .. +63 (4 strips).  The
-// input dimension is walked in steps of BK = 64 (4 tile columns).
+// workgroup (8 waves, one per CU) owns a BM x BN = 256 x 256 block of y (64 x
+// 256 when m <= 64); wave w owns rows BM/2 (w >> 2) .. +BM/2-1 and outputs
+// 64 (w & 3) .. +63 (4 strips).  The input dimension is walked in steps of
+// BK = 64 (4 tile columns).
 //
 // Each weight is decoded once per workgroup and used for 256 rows: of the two
 // waves that own the same outputs (w and w ^ 4, which share a SIMD), one
@@ -26,16 +27,19 @@
 
 namespace exl3 {
 
-constexpr int GM_BM = GEMM_BM;
 constexpr int GM_BN = GEMM_BN;        // 16 strips, 64 outputs per wave
 constexpr int GM_BK = 64;             // 4 tile columns
 constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 bytes)
-constexpr int GM_A_HALVES = GM_BM * GM_LD;
 constexpr int GM_B_FRAGS = 2 * 4 * 4 * 64;  // [k half][output quarter][fragment][lane], 16 bytes each
 
-template <int K, int CB>
+// BM = 256 rows per block (GEMM_BM), or 64 for few rows (m <= 64: the decode of
+// each weight is the work, and a 256-row block would multiply 75 % padding).
+template <int K, int CB, int BM>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
-    __shared__ __align__(16) uint16_t As[2][GM_A_HALVES];
+    constexpr int WR = BM / 2;   // rows per wave
+    constexpr int RF = BM / 32;  // 16-row fragments per wave
+    constexpr int AL = BM / 64;  // x' staging loads per lane per step
+    __shared__ __align__(16) uint16_t As[2][BM * GM_LD];
     __shared__ __align__(16) u32x4_t Bs[2][GM_B_FRAGS];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -48,7 +52,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     const int nbx = gridDim.x, total = gridDim.x * gridDim.y;
     int lin = blockIdx.x + blockIdx.y * nbx;
     if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
-    const int m0 = (lin / nbx) * GM_BM;
+    const int m0 = (lin / nbx) * BM;
     const int s0 = (lin % nbx) * (GM_BN / 16) + 4 * nq;  // first strip of this wave
     // this workgroup's tile columns (split-k): [t0, t1)
     const int t0 = blockIdx.z * p.kz;
@@ -103,43 +107,44 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     };
 
     // ---- x' staging: each load instruction of a wave covers 8 whole rows of the
-    // step (8 lanes x 16 bytes per row), so wave w stages rows 32 w .. 32 w + 31
-    // in 4 loads.  Rows past m read as zero through the buffer range check.
+    // step (8 lanes x 16 bytes per row), so wave w stages rows (BM / 8) w ..
+    // + BM / 8 - 1 in BM / 64 loads.  Rows past m read as zero through the
+    // buffer range check.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.xr + (int64_t)m0 * p.n_in, ((int64_t)p.m - m0) * p.n_in * 2);
-    const int arow = 32 * wave + (lane >> 3), acol = (lane & 7) * 8;  // row of load c: arow + 8c; col in halves
+    const int arow = (BM / 8) * wave + (lane >> 3), acol = (lane & 7) * 8;  // row of load c: arow + 8c; col in halves
     const uint32_t aoff = (uint32_t)arow * p.n_in * 2 + acol * 2;
     const uint32_t arow8 = 8u * p.n_in * 2;  // bytes between the rows of consecutive loads
-    u32x4_t areg[4];
+    u32x4_t areg[AL];
     auto load_a = [&](int tc) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)  // past the end: range check
+        for (int c = 0; c < AL; ++c)  // past the end: range check
             areg[c] = __builtin_bit_cast(u32x4_t,
                                          __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + c * arow8, tc * 32, 0));
     };
     auto store_a = [&](int buf) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < AL; ++c)
             *reinterpret_cast<u32x4_t*>(&As[buf][(arow + 8 * c) * GM_LD + acol]) = areg[c];
     };
 
-    f32x4_t acc[8][4];
+    f32x4_t acc[RF][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < RF; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // 32 inputs (k half kk) of a step: 8 row fragments x 4 output fragments;
+    // 32 inputs (k half kk) of a step: RF row fragments x 4 output fragments;
     // the B fragments of k half kk were decoded by the wave with mh == kk
     auto mfma_half = [&](int buf, int kk) {
         // all 4 B and 8 A fragments of the half are read first: one LDS latency,
         // then 32 back-to-back MFMAs
-        half8_t b[4], af[8];
+        half8_t b[4], af[RF];
 #pragma unroll
         for (int j = 0; j < 4; ++j) b[j] = __builtin_bit_cast(half8_t, Bs[buf][((kk * 4 + nq) * 4 + j) * 64 + lane]);
-        const uint16_t* abase = &As[buf][(128 * mh + n) * GM_LD + 32 * kk + 8 * g];
+        const uint16_t* abase = &As[buf][(WR * mh + n) * GM_LD + 32 * kk + 8 * g];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const half8_t*>(abase + i * 16 * GM_LD);
+        for (int i = 0; i < RF; ++i) af[i] = *reinterpret_cast<const half8_t*>(abase + i * 16 * GM_LD);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < RF; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], b[j], acc[i][j], 0, 0, 0);
@@ -183,7 +188,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
         main_loop(std::integral_constant<int, 0>{});
     else
         main_loop(std::integral_constant<int, 1>{});
-    // D[4g + r][n] of fragment (i, j): row 128 mh + 16i + 4g + r, output 16 (s0 + j) + n
+    // D[4g + r][n] of fragment (i, j): row WR mh + 16i + 4g + r, output 16 (s0 + j) + n
     if (p.zsplit > 1) {  // fp32 partial sums of this split; the reduction scales them
         float* part = p.part + (int64_t)blockIdx.z * p.m * p.n_out;
 #pragma unroll
@@ -191,10 +196,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
             const int o = (s0 + j) * 16 + n;
             if (o >= p.n_out) continue;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int i = 0; i < RF; ++i)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + 128 * mh + i * 16 + 4 * g + r;
+                    const int row = m0 + WR * mh + i * 16 + 4 * g + r;
                     if (row < p.m) part[(int64_t)row * p.n_out + o] = acc[i][j][r];
                 }
         }
@@ -206,10 +211,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
         if (o >= p.n_out) continue;
         const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < RF; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = m0 + 128 * mh + i * 16 + 4 * g + r;
+                const int row = m0 + WR * mh + i * 16 + 4 * g + r;
                 if (row < p.m) p.y[(int64_t)row * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * acc[i][j][r]));
             }
     }
@@ -244,8 +249,13 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
 
 template <int K, int CB>
 static hipError_t launch_gemm_k(const GemmParams& p, hipStream_t s) {
-    dim3 grid((p.n_strips + 15) / 16, (p.m + GM_BM - 1) / GM_BM, p.zsplit);
-    hipLaunchKernelGGL((gemm_kernel<K, CB>), grid, dim3(512), 0, s, p);
+    if (p.m <= GEMM_BM_SMALL) {
+        dim3 grid((p.n_strips + 15) / 16, 1, p.zsplit);
+        hipLaunchKernelGGL((gemm_kernel<K, CB, GEMM_BM_SMALL>), grid, dim3(512), 0, s, p);
+    } else {
+        dim3 grid((p.n_strips + 15) / 16, (p.m + GEMM_BM - 1) / GEMM_BM, p.zsplit);
+        hipLaunchKernelGGL((gemm_kernel<K, CB, GEMM_BM>), grid, dim3(512), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.zsplit <= 1) return e;
     const int64_t groups = (int64_t)p.m * p.n_out / 4;

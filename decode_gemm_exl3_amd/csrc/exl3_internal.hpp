@@ -54,6 +54,7 @@ struct GemmParams {
 };
 
 constexpr int GEMM_BM = 256, GEMM_BN = 256;  // output block of one GEMM workgroup
+constexpr int GEMM_BM_SMALL = 64;            // rows per block when m <= 64
 constexpr int GEMM_MAX_SPLIT = 16;
 constexpr int GEMM_SIZING_CUS = 256;         // CU count the workspace is sized for (MI355X)
 
