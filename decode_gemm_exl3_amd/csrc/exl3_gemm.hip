@@ -1,8 +1,8 @@
 // exl3_gemm.hip - decode-matmul for larger m on the matrix cores (gfx950).
 //
 // The input is rotated once by a pre-pass (x'/128 in fp16, workspace).  A
-// workgroup (8 waves, one per CU) owns a BM x BN = 256 x 256 block of y (64 x
-// 256 when m <= 64); wave w owns rows BM/2 (w >> 2) .. +BM/2-1 and outputs
+// workgroup (8 waves, one per CU) owns a BM x BN = 256 x 256 block of y (64 or
+// 128 x 256 when m <= 64 or 128); wave w owns rows BM/2 (w >> 2) .. +BM/2-1 and outputs
 // 64 (w & 3) .. +63 (4 strips).  The input dimension is walked in steps of
 // BK = 64 (4 tile columns).
 //
@@ -32,8 +32,9 @@ constexpr int GM_BK = 64;             // 4 tile columns
 constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 bytes)
 constexpr int GM_B_FRAGS = 2 * 4 * 4 * 64;  // [k half][output quarter][fragment][lane], 16 bytes each
 
-// BM = 256 rows per block (GEMM_BM), or 64 for few rows (m <= 64: the decode of
-// each weight is the work, and a 256-row block would multiply 75 % padding).
+// BM = 256 rows per block (GEMM_BM), or 64 / 128 for fewer rows (m <= 64 /
+// m <= 128: the decode of each weight is most of the work, and a 256-row block
+// would multiply padding rows).
 template <int K, int CB, int BM>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     constexpr int WR = BM / 2;   // rows per wave
@@ -252,6 +253,9 @@ static hipError_t launch_gemm_k(const GemmParams& p, hipStream_t s) {
     if (p.m <= GEMM_BM_SMALL) {
         dim3 grid((p.n_strips + 15) / 16, 1, p.zsplit);
         hipLaunchKernelGGL((gemm_kernel<K, CB, GEMM_BM_SMALL>), grid, dim3(512), 0, s, p);
+    } else if (p.m <= 2 * GEMM_BM_SMALL) {
+        dim3 grid((p.n_strips + 15) / 16, 1, p.zsplit);
+        hipLaunchKernelGGL((gemm_kernel<K, CB, 2 * GEMM_BM_SMALL>), grid, dim3(512), 0, s, p);
     } else {
         dim3 grid((p.n_strips + 15) / 16, (p.m + GEMM_BM - 1) / GEMM_BM, p.zsplit);
         hipLaunchKernelGGL((gemm_kernel<K, CB, GEMM_BM>), grid, dim3(512), 0, s, p);
