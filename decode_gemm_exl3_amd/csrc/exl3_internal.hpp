@@ -60,14 +60,24 @@ constexpr int GEMM_SIZING_CUS = 256;         // CU count the workspace is sized 
 
 // Split-k plan: split the input dimension while the output blocks alone would
 // leave CUs idle (a medium m gives few blocks), in multiples of 4 tile columns.
+// One GEMM workgroup fills a CU, so the time goes as (rounds of workgroups) x
+// (steps per split + the set-up and write-out of a workgroup, about 3 steps);
+// the split count minimises that, the smallest on ties (fewer partial sums).
 inline void plan_gemm_split(int m, int n_out, int tiles_in, int cus, int* zsplit, int* kz) {
     const int blocks = ((n_out / 16 + 15) / 16) * ((m + GEMM_BM - 1) / GEMM_BM);
-    int z = blocks >= cus ? 1 : (cus + blocks - 1) / blocks;
-    const int steps = tiles_in / 4;
-    if (z > GEMM_MAX_SPLIT) z = GEMM_MAX_SPLIT;
-    if (z > steps) z = steps;
-    if (z < 1) z = 1;
-    const int kstep = (steps + z - 1) / z;  // steps per split
+    const int steps = tiles_in / 4 > 0 ? tiles_in / 4 : 1;
+    int best_z = 1;
+    if (blocks < cus) {
+        long best = -1;
+        for (int z = 1; z <= GEMM_MAX_SPLIT && z <= steps; ++z) {
+            const int kstep = (steps + z - 1) / z;
+            const int zz = (steps + kstep - 1) / kstep;  // splits actually used
+            const long rounds = ((long)blocks * zz + cus - 1) / cus;
+            const long t = rounds * (kstep + 3);
+            if (best < 0 || t < best) { best = t; best_z = zz; }
+        }
+    }
+    const int kstep = (steps + best_z - 1) / best_z;
     *kz = 4 * kstep;
     *zsplit = (steps + kstep - 1) / kstep;
 }
