@@ -31,6 +31,9 @@ int cu_count() {
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 
+// Most rows exl3_linear hands to the GEMV.
+constexpr int GEMV_LINEAR_MAX_M = 12;
+
 // Input length from which a GEMV of 2..8 rows with enough workspace rotates its input in a pre-pass.
 constexpr int GEMV_PREROT_MIN_N_IN = 12288;
 
@@ -326,10 +329,12 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
 int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
                 const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
                 void* workspace, size_t workspace_bytes, void* stream) {
-    // Measured crossover (MI355X, K = 2 and 4; 4096->14336, 14336->4096, 4096->4096):
-    // the GEMV wins while x' of the m rows (4 bytes per input, duplicated fp16)
-    // stays near one LDS chunk, i.e. m * n_in <= 2^17; past it the split GEMM does.
-    const bool use_gemv = m <= EXL3_GEMV_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
+    // Measured crossover (MI355X, K = 4; 4096->14336 and 14336->4096 for
+    // m = 1..16, against the GEMM with 64-row blocks and its split plan): the
+    // GEMV wins through m = 12 at n_in = 4096 and through m = 8 at n_in = 14336
+    // (its x' of the m rows, 4 bytes per input, has to fit the LDS chunks), so
+    // m <= 12 with m * n_in <= 2^17.
+    const bool use_gemv = m <= GEMV_LINEAR_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
     return use_gemv ? exl3_gemv(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream)
                     : exl3_gemm(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream);
 }

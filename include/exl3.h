@@ -170,9 +170,9 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
  * exl3_linear: the same result for any m >= 1, through exl3_gemv or exl3_gemm as
  * a measured table picks (pages: "GEMM kernel" - the kernel map chooses tile
  * sizes and concurrency by architecture and shape; "small-batch GEMV" - small m
- * goes to the GEMV).  The GEMV serves m <= 16 while m * n_in <= 2^17, the GEMM
- * (with its input dimension split across workgroups when the output blocks
- * alone leave compute units idle) the rest.  Arguments and workspace as
+ * goes to the GEMV).  The GEMV serves m <= 12 while m * n_in <= 2^17, the GEMM
+ * (64-, 128- or 256-row blocks by m, its input dimension split across
+ * workgroups when the output blocks alone leave compute units idle) the rest.  Arguments and workspace as
  * exl3_gemm.
  */
 int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
