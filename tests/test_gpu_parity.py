@@ -393,6 +393,17 @@ def test_medium_m_gemv_and_split_gemm(torch_cuda):
         check_workload(torch_cuda, mm, fn, ws)
 
 
+def test_gemm_row_block_boundaries(torch_cuda):
+    # 64-, 128- and 256-row blocks are chosen by m: both sides of each switch,
+    # with split and unsplit input dimensions
+    for n_in, n_out, K in [(1024, 528, 3), (2048, 4112, 4)]:
+        for m in (63, 64, 65, 127, 128, 129):
+            log(f"gemm blocks n_in={n_in} n_out={n_out} K={K} m={m}")
+            words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [23, n_in, m])
+            y = run_linear(torch_cuda, "gemm", words, x, sign, scale, K)
+            assert rel_fro(y, O.linear(x, words, sign, scale, K)) <= TOL, (n_in, n_out, K, m)
+
+
 def test_linear_dispatch(torch_cuda):
     # the measured table: GEMV for small m * n_in, the split GEMM beyond
     for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12)]:
