@@ -14,8 +14,9 @@ value = algorithmic bytes of a step / time of a step (GB/s):
   per launch: K/8 bytes per weight + x (2 m n_in) + sign (2 n_in) once, and
   per projection out_scale (2 n_out) + y (2 m n_out).
 roofline: the dominant kernel (the fused gate+up launch at K=4), algorithmic
-bytes per launch over its average launch time from HIP events around each
-launch.
+bytes per launch over its average launch time from HIP events around a batch
+of back-to-back launches; alu_roofline: the same launch's vector instructions
+(committed counters) against the vector-ALU issue peak.
 cpu_baseline: the CPU oracle on a bounded sample of the same workload.
 
 Prints one JSON line.
@@ -224,13 +225,17 @@ def cpu_baseline():
 
 
 def kernel_sources_hash() -> str:
-    """Hash of the GEMV kernel and launch-plan sources: counter-derived traffic
-    is valid only for them."""
+    """Hash of the GEMV kernel and launch-plan sources with their comments and
+    blank lines removed: counter-derived figures are valid only for this code."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip"):
-        with open(os.path.join(ROOT, "decode_gemm_exl3_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "decode_gemm_exl3_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -11,7 +11,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
-// Optional override of the number of input chunks of a GEMV (tuning sweeps).
+// Integer from the environment, for the tuning overrides (EXL3_GEMV_*, EXL3_GEMM_SPLIT).
 int env_int(const char* name, int dflt) {
     const char* v = getenv(name);
     return (v && *v) ? atoi(v) : dflt;
@@ -39,7 +39,10 @@ constexpr int GEMV_PREROT_MIN_N_IN = 12288;
 
 // Workspace needs.  Nothing in the workspace survives between calls, so each
 // call lays out only what it uses from offset 0:
-//   gemv: nothing (one kernel, partial sums stay in LDS);
+//   gemv: nothing required (one kernel, partial sums stay in LDS); given
+//         m * n_in * 2 bytes it may rotate its input into them once (the
+//         pre-pass), which the GEMM sizing below, the rotated input of max_m
+//         rows, always covers;
 int64_t gemv_ws_bytes(int n_out, int m) { (void)n_out; (void)m; return 0; }
 //   gemm: the rotated input, fp16 [m][n_in], then for a split input dimension
 //         the fp32 partial sums [zsplit][m][n_out].
@@ -52,7 +55,8 @@ int64_t gemm_ws_bytes(int n_in, int n_out, int m, int cus) {
 int64_t ws_total(int n_in, int n_out, int max_m) {
     int64_t best = gemv_ws_bytes(n_out, max_m < EXL3_GEMV_MAX_M ? max_m : EXL3_GEMV_MAX_M);
     // the split depends on m through the number of 256-row blocks: the largest
-    // m of each block count needs the most; past the counts that split, the
+    // m of each block count needs the most; once a block count does not split,
+    // no larger one does (more blocks make splitting less useful), and the
     // rotated input of max_m rows is all
     for (int64_t b = 1; b * exl3::GEMM_BM < (int64_t)max_m + exl3::GEMM_BM; ++b) {
         const int m = (int)(b * exl3::GEMM_BM < max_m ? b * exl3::GEMM_BM : max_m);
