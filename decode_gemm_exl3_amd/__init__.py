@@ -107,6 +107,54 @@ def _ptr(t) -> int:
     return 0 if t is None else t.data_ptr()
 
 
+def _need(t, name: str, dtypes, numel: int | None = None, shape=None) -> None:
+    """The library reads and writes raw device memory: check what it will be
+    handed (contiguous, of the element type and size the call implies; the
+    device is checked by _on_gpu) and raise before anything is launched."""
+    if not hasattr(t, "data_ptr") or not hasattr(t, "is_cuda"):
+        raise Exl3Error(f"{name}: expected a torch tensor")
+    if t.dtype not in dtypes:
+        raise Exl3Error(f"{name}: dtype {t.dtype}, expected one of {tuple(str(d) for d in dtypes)}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise Exl3Error(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise Exl3Error(f"{name}: {t.numel()} elements, expected {numel}")
+    if not t.is_contiguous():
+        raise Exl3Error(f"{name}: must be contiguous")
+
+
+def _on_gpu(**tensors) -> None:
+    """The device check, after the type and size checks of every tensor."""
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise Exl3Error(f"{name}: must be on a GPU device")
+
+
+def _word_dtypes():
+    import torch
+    return tuple(d for d in (torch.int16, getattr(torch, "uint16", None)) if d is not None)
+
+
+def _check_linear(x, trellis, sign, out_scale, bits: int, y, n_outs=None) -> None:
+    import torch
+    if x.dim() != 2:
+        raise Exl3Error(f"x: expected [m, n_in], got shape {tuple(x.shape)}")
+    m, n_in = x.shape
+    _need(x, "x", (torch.float16,))
+    _need(sign, "sign", (torch.float16,), numel=n_in)
+    K = int(bits)
+    pairs = list(zip(trellis, out_scale, y)) if n_outs is not None else [(trellis, out_scale, y)]
+    for i, (tr, sc, yy) in enumerate(pairs):
+        n_out = sc.numel()
+        _need(sc, f"out_scale[{i}]", (torch.float16,))
+        if n_in % 128 == 0 and n_out % 16 == 0 and 1 <= K <= 8:
+            _need(tr, f"trellis[{i}]", _word_dtypes(), numel=(n_out // 16) * (n_in // 16) * 16 * K)
+        _need(yy, f"y[{i}]", (torch.float16,), shape=(m, n_out))
+    _on_gpu(x=x, sign=sign)
+    for i, (tr, sc, yy) in enumerate(pairs):
+        _on_gpu(**{f"trellis[{i}]": tr, f"out_scale[{i}]": sc, f"y[{i}]": yy})
+
+
 def _stream(stream) -> int:
     import torch
     if stream is None:
@@ -136,6 +184,10 @@ def decode_tile(words, bits: int, out=None, stream=None, codebook: int = 0):
     T = words.shape[0]
     if out is None:
         out = torch.empty((T, 256), dtype=torch.float16, device=words.device)
+    if 1 <= int(bits) <= 8:
+        _need(words, "words", _word_dtypes(), numel=T * 16 * int(bits))
+    _need(out, "out", (torch.float16,), numel=T * 256)
+    _on_gpu(words=words, out=out)
     _check(load().exl3_decode_tile(_ptr(words), bits_arg(bits, codebook), T, _ptr(out), _stream(stream)),
            "exl3_decode_tile")
     return out
@@ -147,6 +199,7 @@ def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=N
     n_out = out_scale.shape[0]
     if y is None:
         y = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
+    _check_linear(x, trellis, sign, out_scale, bits, y)
     if workspace is None:
         workspace = Workspace(n_in, n_out, bits, max(m, 1), device=x.device)
     rc = getattr(load(), fn)(_ptr(x), m, _ptr(trellis), _ptr(sign), _ptr(out_scale), n_in, n_out,
@@ -171,6 +224,9 @@ def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None
     n = len(weights)
     if ys is None:
         ys = [torch.empty((m, sc.shape[0]), dtype=torch.float16, device=x.device) for _, sc in weights]
+    if len(ys) != n:
+        raise Exl3Error(f"ys: {len(ys)} outputs for {n} projections")
+    _check_linear(x, [tr for tr, _ in weights], sign, [sc for _, sc in weights], bits, ys, n_outs=True)
     arr = (_Proj * max(n, 1))()
     for i, ((tr, sc), y) in enumerate(zip(weights, ys)):
         arr[i] = _Proj(_ptr(tr), _ptr(sc), _ptr(y), int(sc.shape[0]), 0)
@@ -210,6 +266,12 @@ def encode_tiles(w, bits: int, codebook: int = 0, workspace=None, words=None, co
     if workspace is None:
         workspace = torch.empty(encode_slot_bytes(bits, codebook) * max(1, min(slots, T)), dtype=torch.uint8,
                                 device=w.device)
+    _need(w, "w", (torch.float32,), numel=T * 256)
+    if 1 <= int(bits) <= 8:
+        _need(words, "words", _word_dtypes(), numel=T * 16 * int(bits))
+    _need(costs, "costs", (torch.float32,), numel=T)
+    _need(workspace, "workspace", (torch.uint8,))
+    _on_gpu(w=w, words=words, costs=costs, workspace=workspace)
     rc = load().exl3_encode_tiles(_ptr(w), T, bits_arg(bits, codebook), _ptr(words), _ptr(costs), _ptr(workspace),
                                   workspace.numel(), _stream(stream))
     _check(rc, "exl3_encode_tiles")
