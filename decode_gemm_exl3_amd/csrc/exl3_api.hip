@@ -44,9 +44,16 @@ constexpr int GEMV_PREROT_MIN_N_IN = 12288;
 //         pre-pass), which the GEMM sizing below, the rotated input of max_m
 //         rows, always covers;
 int64_t gemv_ws_bytes(int n_out, int m) { (void)n_out; (void)m; return 0; }
-//   gemm: the rotated input, fp16 [m][n_in], then for a split input dimension
-//         the fp32 partial sums [zsplit][m][n_out].
-int64_t gemm_rot_bytes(int n_in, int m) { return align256((int64_t)m * n_in * 2); }
+//   gemm: the rotated input in fp16, then for a split input dimension the
+//         fp32 partial sums [zsplit][m][n_out].  The rotated input is
+//         row-major [m][n_in] for m <= 128; for the 256-row blocks it is
+//         group-major [n_in / 8][rows][8] over m rounded up to whole blocks
+//         (the padding rows zero).
+bool gemm_group_major(int m) { return m > 2 * exl3::GEMM_BM_SMALL; }
+int64_t gemm_rows(int m) {
+    return gemm_group_major(m) ? ((int64_t)m + exl3::GEMM_BM - 1) / exl3::GEMM_BM * exl3::GEMM_BM : (int64_t)m;
+}
+int64_t gemm_rot_bytes(int n_in, int m) { return align256(gemm_rows(m) * n_in * 2); }
 int64_t gemm_ws_bytes(int n_in, int n_out, int m, int cus) {
     int z = 1, kz = 0;
     exl3::plan_gemm_split(m, n_out, n_in / 16, cus, &z, &kz);
@@ -311,10 +318,12 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
         kz = n_in / 16;
     }
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = exl3::launch_rotate(x, sign, m, n_in, xr, s);
+    const int rows = gemm_group_major(m) ? (int)gemm_rows(m) : 0;
+    hipError_t e = exl3::launch_rotate(x, sign, m, n_in, xr, s, rows);
     if (e != hipSuccess) return EXL3_EHIP;
     exl3::GemmParams p;
     p.xr = xr;
+    p.rows = rows;
     p.trellis = trellis;
     p.out_scale = out_scale;
     p.y = y;

@@ -1,12 +1,15 @@
 // exl3_gemm.hip - decode-matmul for larger m on the matrix cores (gfx950).
 //
-// The input is rotated once by a pre-pass (x'/128 in fp16, workspace).  A
-// workgroup (8 waves, one per CU) owns a BM x BN = 256 x 256 block of y (64 or
-// 128 x 256 when m <= 64 or 128); wave w owns rows BM/2 (w >> 2) .. +BM/2-1 and outputs
+// The input is rotated once by a pre-pass (x'/128 in fp16, workspace).  Two
+// kernels: for m <= 128 an eight-wave workgroup owns a BM x 256 block of y
+// (BM = 64 or 128, below); for m > 128 a four-wave workgroup owns a 256 x 256
+// block (gemm4_kernel, further down).
+//
+// Eight-wave kernel: wave w owns rows BM/2 (w >> 2) .. +BM/2-1 and outputs
 // 64 (w & 3) .. +63 (4 strips).  The input dimension is walked in steps of
 // BK = 64 (4 tile columns).
 //
-// Each weight is decoded once per workgroup and used for 256 rows: of the two
+// Each weight is decoded once per workgroup and used for BM rows: of the two
 // waves that own the same outputs (w and w ^ 4, which share a SIMD), one
 // decodes the first 32 inputs of the step and the other the last 32, each
 // straight into v_mfma B fragments (lane (n, g): half row g & 1 of row n of
@@ -32,9 +35,9 @@ constexpr int GM_BK = 64;             // 4 tile columns
 constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 bytes)
 constexpr int GM_B_FRAGS = 2 * 4 * 4 * 64;  // [k half][output quarter][fragment][lane], 16 bytes each
 
-// BM = 256 rows per block (GEMM_BM), or 64 / 128 for fewer rows (m <= 64 /
-// m <= 128: the decode of each weight is most of the work, and a 256-row block
-// would multiply padding rows).
+// BM = 64 rows per block for m <= 64, 128 for m <= 128 (the decode of each
+// weight is most of the work at such m, and larger blocks would multiply
+// padding rows).
 template <int K, int CB, int BM>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     constexpr int WR = BM / 2;   // rows per wave
@@ -221,6 +224,288 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Row blocks of 256 (m > 128): four waves, one per SIMD.  Wave w owns the
+// outputs of strips 4w .. 4w + 3 of the block (64 outputs) for all 256 rows,
+// so each weight is decoded once per workgroup, by the wave that uses it,
+// straight into its MFMA B operands: no weight goes through LDS.  The 256
+// accumulators per lane (16 row tiles x 4 strips) sit in the accumulation
+// registers.  Only x' is shared, staged in LDS in three buffers.
+//
+// Input order inside a step of 64 inputs (4 tile columns): lane (n, g) of a
+// B operand decodes the whole row n of tile column g (16 weights, the
+// row-owning lane layout of the GEMV) and feeds its first 8 weights to the
+// MFMAs of k half 0 and the last 8 to those of k half 1.  So the MFMA's k
+// slots 8g..8g+7 of half h hold step inputs 16g + 8h .. +7: the 16-byte group
+// 2g + h.  The A operands read the same groups, which the rotation pre-pass
+// lays out group-major (x'[k / 8][row][k % 8]) so that a block's step is 8
+// contiguous 4 KB runs.
+//
+// A step runs its 64 MFMAs of k half 0, then the 64 of k half 1.  During half
+// 0 the wave decodes the half-1 weights of the same step (states 8..15 of its
+// rows); during half 1, the half-0 weights of the next step (states 0..7 of
+// the next rows).  So each B operand is rewritten only after the MFMAs that
+// read it, and one set of B registers serves every step.  A step's rows are
+// loaded once, about a step and a half before their first use, into one of two
+// sets that alternate with the step's parity (the main loop holds two steps).
+// x' is staged two steps ahead (loaded one step earlier) and A fragments are
+// read two row tiles ahead.  Scheduling fences keep each unit of
+// that work next to one MFMA, so the vector ALU work issues while the matrix
+// core runs: with one wave per SIMD nothing else covers a stall.  One barrier
+// per step.
+// ---------------------------------------------------------------------------
+constexpr int G4_BUFS = 3;  // x' buffers in LDS, 32 KB each: [group 8][row 256] x 16 bytes
+
+#define G4_FENCE __builtin_amdgcn_sched_barrier(0)
+
+// v_mad_u32_u16 of the codebook for state c of a finished row (state c at bit
+// cK of b[]): the product word p.  Windows that two states of the same half
+// share (K divides 16) are kept in win[] by the first.
+template <int K, int CB>
+__device__ __forceinline__ uint32_t g4_mad(int c, const uint32_t (&b)[RowGeom<K>::NB], uint32_t (&win)[16],
+                                          const CbRegs& r) {
+    constexpr int NB = RowGeom<K>::NB;
+    constexpr uint32_t A = CB == 0 ? CB_A : CB1_A;
+    const int P = c * K, dw = P >> 5, sh = P & 31;
+    uint32_t w = b[dw];
+    bool hi = false;
+    if (sh == 16) {
+        hi = true;
+    } else if (sh != 0) {
+        const int partner = c - 16 / K;  // state whose window holds this one in its high half
+        if ((16 % K) == 0 && sh > 16 && partner >= (c & 8)) {
+            w = win[partner];
+            hi = true;
+        } else {
+            w = __builtin_amdgcn_alignbit(b[(dw + 1 < NB) ? dw + 1 : dw], b[dw], (uint32_t)sh);
+            win[c] = w;
+        }
+    }
+    uint32_t p;
+    if (hi)
+        asm("v_mad_u32_u16 %0, %1, %2, %3 op_sel:[1,0,0,0]" : "=v"(p) : "v"(w), "s"(A), "v"(r.vB));
+    else
+        asm("v_mad_u32_u16 %0, %1, %2, %3" : "=v"(p) : "v"(w), "s"(A), "v"(r.vB));
+    return p;
+}
+
+// Two values as one fp16x2 dword.  Codebook 0: lo already holds the first
+// value (high half zero); the second is summed from its word straight into the
+// high half (SDWA, the low half preserved): one instruction, not an add, an
+// add and a merge.
+template <int CB>
+__device__ __forceinline__ uint32_t g4_pack(uint32_t lo, uint32_t q1) {
+    if constexpr (CB == 0) {
+        asm("s_nop 0\n\t"
+            "v_add_f16_sdwa %0, %1, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:WORD_0 src1_sel:WORD_1"
+            : "+v"(lo)
+            : "v"(q1));
+        return lo;
+    } else {
+        return cb_pack<CB>(lo, q1);
+    }
+}
+
+// D += A B with D in accumulation registers.  In assembly so that the
+// register allocator keeps all 256 accumulators in place (with the builtin it
+// moves them between register files every step).  The compiler does not see
+// this MFMA, so the schedule keeps its hazards away: every B operand is
+// written by the vector ALU at least two MFMAs before it is read, A operands
+// come from LDS (the wait counts see the asm operands), and the accumulators
+// are read only after the main loop, behind explicit wait states.
+__device__ __forceinline__ void g4_mfma(f32x4_t& d, const half8_t& a, const u32x4_t& b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
+}
+
+template <int K, int CB>
+__global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
+    __shared__ __align__(16) u32x4_t As[G4_BUFS * 8 * 256];
+    constexpr int NB = RowGeom<K>::NB;
+    constexpr uint32_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int n = lane & 15, g = lane >> 4;
+    // XCD-aware block order (as the eight-wave kernel)
+    const int nbx = gridDim.x, total = gridDim.x * gridDim.y;
+    int lin = blockIdx.x + blockIdx.y * nbx;
+    if ((total & 7) == 0) lin = (lin & 7) * (total >> 3) + (lin >> 3);
+    const int m0 = (lin / nbx) * GEMM_BM;
+    const int s0 = (lin % nbx) * (GEMM_BN / 16) + 4 * wave;  // first strip of this wave
+    const int k0 = blockIdx.z * (p.kz / 4);                   // steps of this split: [k0, k1)
+    const int k1 = min(p.tiles_in / 4, k0 + p.kz / 4);
+    const CbRegs cr = cb_regs<CB>();
+
+    // weights: lane (n, g) loads row n of tile column 4 ks + g of strips s0 .. s0 + 3.
+    // Strips past the end and steps past the last read as zero or as other
+    // weights; neither reaches an output that is written.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.trellis, (int64_t)p.n_strips * p.tiles_in * TILE_B);
+    const uint32_t voff = (uint32_t)g * TILE_B + row_offset<K>(n);
+    const uint32_t strip_b = (uint32_t)p.tiles_in * TILE_B;
+    uint32_t rows[2][4][NB];  // [step parity][strip]
+    uint32_t bq[2][4][4];     // B operands [k half][strip]
+    auto load_rows = [&](uint32_t (&rr)[4][NB], int j, int ks) {
+        load_row<K>(rs, voff, (uint32_t)(s0 + j) * strip_b + (uint32_t)ks * 4 * TILE_B, rr[j]);
+    };
+
+    // x': thread t stages row m0 + t of the block, 8 groups of 16 bytes per step
+    const int64_t xrows = p.rows;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.xr, xrows * p.n_in * 2);
+    const uint32_t aoff = (uint32_t)(m0 + tid) * 16;
+    const uint32_t agrp = (uint32_t)xrows * 16;  // bytes between groups
+    u32x4_t areg[8];
+    auto load_a = [&](int c, int ks) {
+        areg[c] = __builtin_bit_cast(u32x4_t,
+                                     __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, (uint32_t)(ks * 8 + c) * agrp, 0));
+    };
+    // fragment (row tile rt, k half h) of a buffer: lane (n, g) reads group 2g + h of row 16 rt + n
+    const int afrag = 2 * g * 256 + n;
+
+    f32x4_t acc[16][4];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- prologue: x' of steps k0 and k0 + 1 in buffers 0 and 1, step k0 + 2
+    // in registers; half 0 of step k0 decoded from rows[0] (finished), rows[1]
+    // hold step k0 + 1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_rows(rows[0], j, k0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) load_rows(rows[1], j, k0 + 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) load_a(c, k0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) As[c * 256 + tid] = areg[c];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) load_a(c, k0 + 1);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) As[2048 + c * 256 + tid] = areg[c];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) load_a(c, k0 + 2);
+    {
+        uint32_t win[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            finish_row<K>(n, rows[0][j]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t pa = g4_mad<K, CB>(2 * e, rows[0][j], win, cr);
+                const uint32_t pb = g4_mad<K, CB>(2 * e + 1, rows[0][j], win, cr);
+                bq[0][j][e] = cb_pack<CB>(cb_word<CB>(pa, cr), cb_word<CB>(pb, cr));
+            }
+        }
+    }
+    __syncthreads();
+    half8_t ar[4];  // A fragments, ring of row tiles
+#pragma unroll
+    for (int t = 0; t < 2; ++t) ar[t] = __builtin_bit_cast(half8_t, As[afrag + t * 16]);
+
+    // ---- one step ks: buffers bc (x' of ks), bn (ks + 1), bs (gets ks + 2).
+    // rows[P] hold step ks (finished), rows[P ^ 1] step ks + 1.
+    auto step = [&](int ks, int bc, int bn, int bs, auto par) {
+        constexpr int P = decltype(par)::value;
+        const u32x4_t* acur = As + bc * 2048 + afrag;
+        const u32x4_t* anext = As + bn * 2048 + afrag;
+        u32x4_t* ast = As + bs * 2048 + tid;
+        uint32_t win[16];
+        uint32_t pa = 0, pb = 0, qa = 0, qb = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // half 0 decodes states 8..15 of rows[P] (step ks) into bq[1] and
+            // then reloads them with step ks + 2; half 1 finishes rows[P ^ 1]
+            // (step ks + 1) and decodes its states 0..7 into bq[0]
+            uint32_t (&rr)[4][NB] = h == 0 ? rows[P] : rows[P ^ 1];
+#pragma unroll
+            for (int rt = 0; rt < 16; ++rt) {
+                {  // fragment two row tiles ahead: (rt + 2, h), then (rt - 14, 1), then the next step's (rt - 14, 0)
+                    const int t2 = rt + 2;
+                    const u32x4_t* src = (h == 1 && t2 >= 16) ? anext : acur;
+                    const int hh = t2 >= 16 ? h ^ 1 : h;
+                    ar[t2 & 3] = __builtin_bit_cast(half8_t, src[hh * 256 + (t2 & 15) * 16]);
+                }
+                G4_FENCE;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int idx = 4 * rt + j;
+                    const u32x4_t bv = u32x4_t{bq[h][j][0], bq[h][j][1], bq[h][j][2], bq[h][j][3]};
+                    g4_mfma(acc[rt][j], ar[rt & 3], bv);
+                    // decode unit idx: strip sd, state pair pr, kind
+                    const int sd = idx >> 4, pr = (idx >> 2) & 3, kind = idx & 3;
+                    const int c0 = (h == 0 ? 8 : 0) + 2 * pr;
+                    uint32_t (&b)[NB] = rr[sd];
+                    if (kind == 0) {
+                        if (h == 1 && pr == 0) finish_row<K>(n, b);
+                        pa = g4_mad<K, CB>(c0, b, win, cr);
+                    } else if (kind == 1) {
+                        pb = g4_mad<K, CB>(c0 + 1, b, win, cr);
+                    } else if (kind == 2) {
+                        qa = cb_word<CB>(pa, cr);
+                        qb = cb_word<CB>(pb, cr);
+                        if constexpr (CB == 0) qa = cb_sum(qa);  // first value, high half zero
+                    } else {
+                        bq[h ^ 1][sd][pr] = g4_pack<CB>(qa, qb);
+                        if (h == 0 && pr == 3) load_rows(rr, sd, ks + 2);  // the row is decoded: refill
+                    }
+                    if (h == 0 && j == 1 && rt < 8) {  // x' group rt: registers to LDS, then step ks + 3's
+                        ast[rt * 256] = areg[rt];
+                        load_a(rt, ks + 3);
+                    }
+                    G4_FENCE;
+                }
+            }
+        }
+        __syncthreads();
+    };
+
+    int ks = k0, bc = 0, bn = 1, bs = 2;
+    for (; ks + 1 < k1; ks += 2) {
+        step(ks, bc, bn, bs, std::integral_constant<int, 0>{});
+        step(ks + 1, bn, bs, bc, std::integral_constant<int, 1>{});
+        const int t = bc;  // rotate the buffers by two steps
+        bc = bs;
+        bs = bn;
+        bn = t;
+    }
+    if (ks < k1) step(ks, bc, bn, bs, std::integral_constant<int, 0>{});
+    // the last MFMAs' results: 8-pass writes need 11 wait states before a read
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+
+    // D[4g + r][n] of (rt, j): row m0 + 16 rt + 4g + r, output 16 (s0 + j) + n
+    if (p.zsplit > 1) {
+        float* part = p.part + (int64_t)blockIdx.z * p.m * p.n_out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int o = (s0 + j) * 16 + n;
+            if (o >= p.n_out) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m0 + i * 16 + 4 * g + r;
+                    if (row < p.m) part[(int64_t)row * p.n_out + o] = acc[i][j][r];
+                }
+        }
+        return;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int o = (s0 + j) * 16 + n;
+        if (o >= p.n_out) continue;
+        const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + i * 16 + 4 * g + r;
+                if (row < p.m) p.y[(int64_t)row * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * acc[i][j][r]));
+            }
+    }
+}
+#undef G4_FENCE
+
+
 // Split-k reduction: y[r][o] = fp16(out_scale[o] * 128 * sum_z part[z][r][o]),
 // the splits added in order.  Four outputs per thread (n_out % 16 == 0).
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part,
@@ -257,8 +542,9 @@ static hipError_t launch_gemm_k(const GemmParams& p, hipStream_t s) {
         dim3 grid((p.n_strips + 15) / 16, 1, p.zsplit);
         hipLaunchKernelGGL((gemm_kernel<K, CB, 2 * GEMM_BM_SMALL>), grid, dim3(512), 0, s, p);
     } else {
-        dim3 grid((p.n_strips + 15) / 16, (p.m + GEMM_BM - 1) / GEMM_BM, p.zsplit);
-        hipLaunchKernelGGL((gemm_kernel<K, CB, GEMM_BM>), grid, dim3(512), 0, s, p);
+        if (p.rows < p.m || p.rows % GEMM_BM != 0) return hipErrorInvalidValue;  // group-major x' required
+        dim3 grid((p.n_strips + 15) / 16, p.rows / GEMM_BM, p.zsplit);
+        hipLaunchKernelGGL((gemm4_kernel<K, CB>), grid, dim3(256), 0, s, p);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.zsplit <= 1) return e;

@@ -40,7 +40,8 @@ __host__ __device__ inline size_t gemv_lds_bytes(int m, int waves, int nsw, int 
 }
 
 struct GemmParams {
-    const uint16_t* xr;     // rotated input, fp16 [m][n_in] (x'/128)
+    const uint16_t* xr;     // rotated input x'/128 in fp16: [m][n_in], or [n_in / 8][rows][8] when rows > 0
+    int rows;               // rows of the group-major layout (m rounded up to the row block), or 0
     const uint16_t* trellis;
     const uint16_t* out_scale;
     uint16_t* y;
@@ -97,8 +98,9 @@ hipError_t launch_encode(int K, int cb, const EncodeParams& p, int grid, hipStre
 
 // cb selects the codebook: 0 (multiply, mask-and-plant, half sum) or 1 (byte sum)
 hipError_t launch_decode(int K, int cb, const uint16_t* words, int64_t n_tiles, uint16_t* out, hipStream_t s);
+// rows == 0: row-major xr[m][n_in]; rows > 0: xr[n_in / 8][rows][8], rows m.. zero
 hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr,
-                         hipStream_t s);
+                         hipStream_t s, int rows = 0);
 hipError_t launch_gemv(int K, int cb, const GemvParams& p, hipStream_t s);
 hipError_t launch_gemm(int K, int cb, const GemmParams& p, hipStream_t s);
 

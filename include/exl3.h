@@ -159,8 +159,9 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
  * with a tiled matrix product).  Arguments and workspace rules as exl3_gemv;
  * the workspace holds the rotated input and, when the input dimension is split
  * across workgroups (few output blocks), fp32 partial sums: a workspace of the
- * size exl3_pack_info gives always suffices, a smaller one (at least m*n_in*2
- * bytes, rounded up to 256) splits less.
+ * size exl3_pack_info gives always suffices, a smaller one (at least
+ * rows*n_in*2 bytes rounded up to 256, with rows = m for m <= 128 and m rounded
+ * up to a multiple of 256 beyond) splits less.
  */
 int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,

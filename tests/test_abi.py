@@ -43,6 +43,10 @@ def test_pack_info_sizes(lib):
         assert info["trellis_bytes"] == n_in * n_out * K // 8 == 2 * info["trellis_words"]
         assert info["workspace_bytes"] >= mm * n_in * 2              # gemm: rotated input
     assert ex.pack_info(4096, 4096, 4, 1)["workspace_bytes"] < ex.pack_info(4096, 4096, 4, 64)["workspace_bytes"]
+    # beyond 128 rows the GEMM stages its rotated input in whole 256-row blocks
+    for mm in (129, 300, 513):
+        rows = (mm + 255) // 256 * 256
+        assert ex.pack_info(1024, 4096, 4, mm)["workspace_bytes"] >= rows * 1024 * 2
 
 
 @pytest.mark.parametrize("args", [(100, 16, 4, 1), (128, 17, 4, 1), (128, 16, 0, 1), (128, 16, 9, 1),

@@ -404,6 +404,23 @@ def test_gemm_row_block_boundaries(torch_cuda):
             assert rel_fro(y, O.linear(x, words, sign, scale, K)) <= TOL, (n_in, n_out, K, m)
 
 
+@pytest.mark.parametrize("K", range(1, 9))
+def test_gemm_256_row_blocks(torch_cuda, K):
+    # the four-wave 256-row kernel (m > 128): ragged and whole row blocks, output
+    # counts that leave a block partly empty, both codebooks, and the input
+    # dimension split into 1-step pieces (the main loop's one-step tail only),
+    # into two 5-step pieces (two passes of the two-step loop, then the tail) and
+    # not split (256 blocks, one pass of the loop)
+    for n_in, n_out, m, cb in [(128, 272, 129, 0), (384, 48, 256, 1), (1024, 528, 513, 1),
+                               (640, 4096, 2048, 0), (128, 4096, 4096, 1)]:
+        log(f"gemm 256-row blocks K={K} n_in={n_in} n_out={n_out} m={m} codebook={cb}")
+        words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [29, K, n_in, m])
+        y = run_linear(torch_cuda, "gemm", words, x, sign, scale, K, cb=cb)
+        assert np.isfinite(y).all()
+        err = rel_fro(y, O.linear(x, words, sign, scale, K, cb=cb))
+        assert err <= TOL, (K, n_in, n_out, m, cb, err)
+
+
 def test_linear_dispatch(torch_cuda):
     # the measured table: GEMV for small m * n_in, the split GEMM beyond
     for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12)]:
