@@ -168,11 +168,12 @@ def copy_bandwidth(torch, nbytes=1 << 30, iters=10):
     return 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
-def gemm_tflops(torch, ex, iters=5, codebook=0):
-    """Prefill GEMM: m=2048, 8192->8192 at K=4 (context figure for the second metric)."""
+def gemm_tflops(torch, ex, iters=5, codebook=0, n_out=8192, K=4):
+    """Prefill GEMM: m=2048, 8192->8192 at K=4, or 8192->n_out at K (the second metric)."""
     import synth
-    m, n_in, n_out, K = 2048, 8192, 8192, 4
-    w = torch.from_numpy(synth.words_only(n_in, n_out, K, [0, 4, 9]).view(np.int16)).cuda()
+    m, n_in = 2048, 8192
+    w = torch.from_numpy(synth.words_only(n_in, n_out, K, [0, 4, 9] if (n_out, K) == (8192, 4) else [0, K, 9, n_out])
+                         .view(np.int16)).cuda()
     x = torch.randn((m, n_in), device="cuda").half()
     sign = torch.ones(n_in, dtype=torch.float16, device="cuda")
     scale = torch.full((n_out,), 0.02, dtype=torch.float16, device="cuda")
@@ -189,6 +190,28 @@ def gemm_tflops(torch, ex, iters=5, codebook=0):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     return 2.0 * m * n_in * n_out / (ms * 1e-3) / 1e12, ms
+
+
+def fp16_matmul_tflops(torch, iters=10):
+    """Context for the GEMM: a plain fp16 matrix product of the same shape
+    (2048 x 8192 by 8192 x 8192, no decode) through torch's BLAS on the same
+    GPU: what the vendor library reaches on this part, at the clock the matrix
+    cores hold on random data."""
+    m, k, n = 2048, 8192, 8192
+    a = torch.randn((m, k), device="cuda").half()
+    b = torch.randn((k, n), device="cuda").half()
+    c = a @ b
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del a, b, c
+    return 2.0 * m * k * n / (ms * 1e-3) / 1e12, ms
 
 
 def cpu_baseline():
@@ -393,9 +416,14 @@ def encode_rates(torch, ex, n_tiles=2048, Ks=(2, 3, 4)):
 
 def only_mode(what, steps, replicas):
     """Short runs for the profiler: the fused gate+up launch at K=4 alone (the
-    dominant kernel), or a plain copy of known size."""
+    dominant kernel), the m=2048 8192->8192 K=4 GEMM, or a plain copy of known
+    size."""
     import torch
     import decode_gemm_exl3_amd as ex
+    if what == "gemm":
+        tf, ms = gemm_tflops(torch, ex, iters=steps)
+        print(json.dumps({"gemm_m2048_8192x8192_k4": {"launches": steps + 1, "tflops": round(tf, 1)}}), flush=True)
+        return
     if what == "copy":
         nbytes = 256 << 20
         a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
@@ -421,7 +449,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=7)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="headline line only (no m=4/8, GEMM, 70B, stack)")
-    ap.add_argument("--only", choices=["gate_up_k4", "copy"], help="profiling runs: one launch shape only")
+    ap.add_argument("--only", choices=["gate_up_k4", "gemm", "copy"], help="profiling runs: one launch shape only")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
@@ -466,8 +494,14 @@ def main():
             del calls
             torch.cuda.empty_cache()
         tf, gms = gemm_tflops(torch, ex)
+        tfr, rms = fp16_matmul_tflops(torch)
         extra["gemm_m2048_8192x8192_k4"] = {"tflops": round(tf, 1), "ms": round(gms, 3),
-                                            "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+                                            "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                            "plain_fp16_matmul_same_shape": {"tflops": round(tfr, 1),
+                                                                             "ms": round(rms, 3)}}
+        tf3, gms3 = gemm_tflops(torch, ex, n_out=28672, K=3)
+        extra["gemm_m2048_8192x28672_k3"] = {"tflops": round(tf3, 1), "ms": round(gms3, 3),
+                                             "frac_of_mfma_f16_peak": round(tf3 / MFMA_F16_PEAK_TFLOPS, 4)}
         extra["llama70b_m1"] = llama70b_rates(torch, ex)
         extra["encode"] = encode_rates(torch, ex)
         extra["medium_m_4096x14336_k4"] = medium_m(torch, ex)

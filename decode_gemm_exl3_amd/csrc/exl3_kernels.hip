@@ -143,16 +143,13 @@ __device__ __forceinline__ uint32_t pack_half2(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
-// rotate: fp16((H128 (sign * x[r]))[k] / 128) for every row r < m and input k.
-// 16 lanes per block, 8 inputs per lane (one 16-byte load and store); a
-// workgroup covers 16 blocks of a row (blockIdx.x) and walks rows blockIdx.y,
-// + gridDim.y, ...  Output layout: row-major xr[r][k] when rows == 0, else
-// groups of 8 inputs outermost, xr[k / 8][r][k % 8] over `rows` >= m rows, the
-// rows past m zero (the GEMM's staging layout: one 16-byte group of each row).
+// rotate: xr[r][k] = fp16((H128 (sign * x[r]))[k] / 128).  16 lanes per block,
+// 8 inputs per lane (one 16-byte load and store); a workgroup covers 16
+// blocks of a row (blockIdx.x) and walks rows blockIdx.y, + gridDim.y, ...
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ sign, int m, int n_in,
-                                                     uint16_t* __restrict__ xr, int rows) {
+                                                     uint16_t* __restrict__ xr) {
     const int l16 = threadIdx.x & 15;
     const int bb = blockIdx.x * 16 + (threadIdx.x >> 4);  // 128-input block within the row
     // whole rows of 16 lanes leave together, so the DPP rows stay complete
@@ -160,21 +157,50 @@ __global__ __launch_bounds__(256) void rotate_kernel(const uint16_t* __restrict_
     const int col = bb * 128 + l16 * 8;
     const RowFwht k = row_fwht_consts(l16);
     const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(sign + col);
-    const int kg = bb * 16 + k.pos;  // group of 8 outputs this lane writes
-    const int rows_out = rows > 0 ? rows : m;
-    for (int row = blockIdx.y; row < rows_out; row += gridDim.y) {
-        u32x4_t o = u32x4_t{0u, 0u, 0u, 0u};
-        if (row < m) {  // uniform per workgroup
-            const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + (int64_t)row * n_in + col);
-            float v[8];
-            row_load_pairs(xv, sv, v);
-            fwht128_row(v, k);
+    for (int row = blockIdx.y; row < m; row += gridDim.y) {
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + (int64_t)row * n_in + col);
+        float v[8];
+        row_load_pairs(xv, sv, v);
+        fwht128_row(v, k);
+        u32x4_t o;
 #pragma unroll
-            for (int d = 0; d < 4; ++d) o[d] = pack_half2(v[2 * d] * k.osc, v[2 * d + 1] * k.osc);
-        }
-        const int64_t at = rows > 0 ? ((int64_t)kg * rows + row) * 8 : (int64_t)row * n_in + kg * 8;
-        *reinterpret_cast<u32x4_t*>(xr + at) = o;
+        for (int d = 0; d < 4; ++d) o[d] = pack_half2(v[2 * d] * k.osc, v[2 * d + 1] * k.osc);
+        *reinterpret_cast<u32x4_t*>(xr + (int64_t)row * n_in + bb * 128 + k.pos * 8) = o;
     }
+}
+
+// ---------------------------------------------------------------------------
+// rotate, group-major: the same values laid out xr[k / 8][r][k % 8] over
+// `rows` >= m rows, the rows past m zero (the 256-row GEMM stages one 16-byte
+// group of each row).  A workgroup rotates one 128-input block (blockIdx.x) of
+// 16 rows (blockIdx.y), one row per 16 lanes, and transposes through LDS so
+// that each group of 8 outputs leaves as one 256-byte run of 16 rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rotate_gm_kernel(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ sign, int m, int n_in,
+                                                        uint16_t* __restrict__ xr, int rows) {
+    __shared__ u32x4_t T[16][16];  // [group of the block][row]
+    const int l16 = threadIdx.x & 15, rr = threadIdx.x >> 4;
+    const int bb = blockIdx.x;
+    const int row = blockIdx.y * 16 + rr;
+    const RowFwht k = row_fwht_consts(l16);
+    u32x4_t o = u32x4_t{0u, 0u, 0u, 0u};
+    if (row < m) {  // whole 16-lane rows agree, so the DPP rows stay complete
+        const int col = bb * 128 + l16 * 8;
+        const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(sign + col);
+        const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(x + (int64_t)row * n_in + col);
+        float v[8];
+        row_load_pairs(xv, sv, v);
+        fwht128_row(v, k);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) o[d] = pack_half2(v[2 * d] * k.osc, v[2 * d + 1] * k.osc);
+    }
+    T[k.pos][rr] = o;
+    __syncthreads();
+    const int g = threadIdx.x >> 4, r = threadIdx.x & 15;  // write side: group g, row r
+    const int orow = blockIdx.y * 16 + r;
+    if (orow < rows)
+        *reinterpret_cast<u32x4_t*>(xr + ((int64_t)(bb * 16 + g) * rows + orow) * 8) = T[g][r];
 }
 
 // ---------------------------------------------------------------------------
@@ -420,10 +446,15 @@ hipError_t launch_decode(int K, int cb, const uint16_t* words, int64_t n_tiles, 
 
 hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_in, uint16_t* xr, hipStream_t s,
                          int rows) {
-    const int rr = rows > 0 ? rows : m;
+    if (rows > 0) {
+        if (rows < m || rows % 16 != 0 || rows / 16 > 65535) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(rotate_gm_kernel, dim3((unsigned)(n_in >> 7), (unsigned)(rows / 16)), dim3(256), 0, s, x,
+                           sign, m, n_in, xr, rows);
+        return hipGetLastError();
+    }
     const unsigned gx = (unsigned)(((n_in >> 7) + 15) / 16);
-    const unsigned gy = (unsigned)(rr < 65535 ? rr : 65535);
-    hipLaunchKernelGGL(rotate_kernel, dim3(gx, gy), dim3(256), 0, s, x, sign, m, n_in, xr, rows);
+    const unsigned gy = (unsigned)(m < 65535 ? m : 65535);
+    hipLaunchKernelGGL(rotate_kernel, dim3(gx, gy), dim3(256), 0, s, x, sign, m, n_in, xr);
     return hipGetLastError();
 }
 
