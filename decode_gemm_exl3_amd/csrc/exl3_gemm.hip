@@ -230,7 +230,7 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
 // so each weight is decoded once per workgroup, by the wave that uses it,
 // straight into its MFMA B operands: no weight goes through LDS.  The 256
 // accumulators per lane (16 row tiles x 4 strips) sit in the accumulation
-// registers.  Only x' is shared, staged in LDS in three buffers.
+// registers.  Only x' is shared, staged in LDS in four buffers.
 //
 // Input order inside a step of 64 inputs (4 tile columns): lane (n, g) of a
 // B operand decodes the whole row n of tile column g (16 weights, the
@@ -248,13 +248,14 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
 // read it, and one set of B registers serves every step.  A step's rows are
 // loaded once, about a step and a half before their first use, into one of two
 // sets that alternate with the step's parity (the main loop holds two steps).
-// x' is staged two steps ahead (loaded one step earlier) and A fragments are
-// read two row tiles ahead.  Scheduling fences keep each unit of
-// that work next to one MFMA, so the vector ALU work issues while the matrix
-// core runs: with one wave per SIMD nothing else covers a stall.  One barrier
-// per step.
+// x' goes from memory straight into LDS (buffer loads to LDS, no registers)
+// three steps ahead, into the fourth of four buffers; the barrier that ends a
+// step waits only for the loads issued a step earlier.  A fragments are read
+// two row tiles ahead.  Scheduling fences keep each unit of that work next to
+// one MFMA, so the vector ALU work issues while the matrix core runs: with one
+// wave per SIMD nothing else covers a stall.  One barrier per step.
 // ---------------------------------------------------------------------------
-constexpr int G4_BUFS = 3;  // x' buffers in LDS, 32 KB each: [group 8][row 256] x 16 bytes
+constexpr int G4_BUFS = 4;  // x' buffers in LDS, 32 KB each: [group 8][row 256] x 16 bytes
 
 #define G4_FENCE __builtin_amdgcn_sched_barrier(0)
 
@@ -348,15 +349,18 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
         load_row<K>(rs, voff, (uint32_t)(s0 + j) * strip_b + (uint32_t)ks * 4 * TILE_B, rr[j]);
     };
 
-    // x': thread t stages row m0 + t of the block, 8 groups of 16 bytes per step
+    // x': wave w stages groups 2w and 2w + 1 of a step, 64 rows per load,
+    // straight from memory into LDS (buffer loads to LDS: M0 holds the wave's
+    // destination, lane i writes 16 bytes at +16 i)
     const int64_t xrows = p.rows;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.xr, xrows * p.n_in * 2);
-    const uint32_t aoff = (uint32_t)(m0 + tid) * 16;
+    const uint32_t avoff = (uint32_t)(m0 + lane) * 16;
     const uint32_t agrp = (uint32_t)xrows * 16;  // bytes between groups
-    u32x4_t areg[8];
-    auto load_a = [&](int c, int ks) {
-        areg[c] = __builtin_bit_cast(u32x4_t,
-                                     __builtin_amdgcn_raw_buffer_load_b128(ra, aoff, (uint32_t)(ks * 8 + c) * agrp, 0));
+    auto stage_a = [&](int i, int ks, int buf) {  // load i of 8: group 2w + (i >> 2), rows 64 (i & 3) ..
+        const int c = 2 * wave + (i >> 2), q = i & 3;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(As + buf * 2048 + c * 256 + q * 64), 16,
+            avoff + (uint32_t)q * 1024, (uint32_t)(ks * 8 + c) * agrp, 0, 0);
     };
     // fragment (row tile rt, k half h) of a buffer: lane (n, g) reads group 2g + h of row 16 rt + n
     const int afrag = 2 * g * 256 + n;
@@ -375,15 +379,9 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) load_rows(rows[1], j, k0 + 1);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) load_a(c, k0);
+    for (int t = 0; t < 3; ++t)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) As[c * 256 + tid] = areg[c];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) load_a(c, k0 + 1);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) As[2048 + c * 256 + tid] = areg[c];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) load_a(c, k0 + 2);
+        for (int i = 0; i < 8; ++i) stage_a(i, k0 + t, t);
     {
         uint32_t win[16];
 #pragma unroll
@@ -397,18 +395,23 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
             }
         }
     }
+    // every load of the prologue, the staging of steps k0 .. k0 + 2 included,
+    // has landed (the steps' own waits count only their loads)
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0)
     __syncthreads();
     half8_t ar[4];  // A fragments, ring of row tiles
 #pragma unroll
     for (int t = 0; t < 2; ++t) ar[t] = __builtin_bit_cast(half8_t, As[afrag + t * 16]);
 
-    // ---- one step ks: buffers bc (x' of ks), bn (ks + 1), bs (gets ks + 2).
-    // rows[P] hold step ks (finished), rows[P ^ 1] step ks + 1.
-    auto step = [&](int ks, int bc, int bn, int bs, auto par) {
+    // ---- one step ks: buffers (ks - k0) % 4 hold x' of ks, + 1 of ks + 1 (+ 2
+    // of ks + 2, landing), + 3 gets ks + 3.  rows[P] hold step ks (finished),
+    // rows[P ^ 1] step ks + 1.
+    auto step = [&](int ks, auto par) {
         constexpr int P = decltype(par)::value;
-        const u32x4_t* acur = As + bc * 2048 + afrag;
-        const u32x4_t* anext = As + bn * 2048 + afrag;
-        u32x4_t* ast = As + bs * 2048 + tid;
+        const int b0 = (ks - k0) & 3;
+        const u32x4_t* acur = As + b0 * 2048 + afrag;
+        const u32x4_t* anext = As + ((b0 + 1) & 3) * 2048 + afrag;
+        const int bs = (b0 + 3) & 3;
         uint32_t win[16];
         uint32_t pa = 0, pb = 0, qa = 0, qb = 0;
 #pragma unroll
@@ -448,27 +451,24 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
                         bq[h ^ 1][sd][pr] = g4_pack<CB>(qa, qb);
                         if (h == 0 && pr == 3) load_rows(rr, sd, ks + 2);  // the row is decoded: refill
                     }
-                    if (h == 0 && j == 1 && rt < 8) {  // x' group rt: registers to LDS, then step ks + 3's
-                        ast[rt * 256] = areg[rt];
-                        load_a(rt, ks + 3);
-                    }
+                    if (h == 0 && j == 1 && rt < 8) stage_a(rt, ks + 3, bs);
                     G4_FENCE;
                 }
             }
         }
-        __syncthreads();
+        // x' of step ks + 2 (this wave's loads of the previous step) has landed:
+        // only the 15 memory loads issued after them (3 row loads of the
+        // previous step, the 12 loads of this one) may still be in flight
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 15);  // vmcnt(15)
+        __builtin_amdgcn_s_barrier();
     };
 
-    int ks = k0, bc = 0, bn = 1, bs = 2;
+    int ks = k0;
     for (; ks + 1 < k1; ks += 2) {
-        step(ks, bc, bn, bs, std::integral_constant<int, 0>{});
-        step(ks + 1, bn, bs, bc, std::integral_constant<int, 1>{});
-        const int t = bc;  // rotate the buffers by two steps
-        bc = bs;
-        bs = bn;
-        bn = t;
+        step(ks, std::integral_constant<int, 0>{});
+        step(ks + 1, std::integral_constant<int, 1>{});
     }
-    if (ks < k1) step(ks, bc, bn, bs, std::integral_constant<int, 0>{});
+    if (ks < k1) step(ks, std::integral_constant<int, 0>{});
     // the last MFMAs' results: 8-pass writes need 11 wait states before a read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
