@@ -371,9 +371,8 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ---- prologue: x' of steps k0 and k0 + 1 in buffers 0 and 1, step k0 + 2
-    // in registers; half 0 of step k0 decoded from rows[0] (finished), rows[1]
-    // hold step k0 + 1
+    // ---- prologue: x' of steps k0 .. k0 + 2 into buffers 0 .. 2; half 0 of
+    // step k0 decoded from rows[0] (finished), rows[1] hold step k0 + 1
 #pragma unroll
     for (int j = 0; j < 4; ++j) load_rows(rows[0], j, k0);
 #pragma unroll
