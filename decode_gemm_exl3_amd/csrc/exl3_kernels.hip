@@ -295,7 +295,6 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         for (int u = 0; u < PF; ++u) load_row<K>(s0.rs, loff, min(s0.off + u * STEP_B, s0.lim), buf[u]);
     }
     for (int i = tid; i < PF * 64; i += 64 * W) zero[i] = 0u;
-    for (int i = tid; i < nj * W * M * 16; i += 64 * W) red[i] = 0.f;
 
     const bool adata = n < M;
     const CbRegs cr = cb_regs<CB>();
@@ -392,11 +391,19 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
             };
             round(0, std::true_type{});
             for (int st = PF; st < nsw; st += PF) round(st, std::false_type{});
-            // this wave's partial for strip j (its own slots: no barrier needed)
+            // this wave's partial for strip j (its own slots: no barrier needed);
+            // the first chunk writes every slot, later chunks add to it
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * g + i;
-                if (r < M) red[((j * W + wave) * M + r) * 16 + n] += (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+                if (r < M) {
+                    const float v = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+                    float* slot = red + ((j * W + wave) * M + r) * 16 + n;
+                    if (c == 0)
+                        *slot = v;
+                    else
+                        *slot += v;
+                }
             }
             cur = nxt;
         }
