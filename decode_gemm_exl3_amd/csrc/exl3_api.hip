@@ -177,12 +177,18 @@ bool bad_shape(int32_t n_in, int32_t n_out, int32_t bits) {
     return n_in <= 0 || n_out <= 0 || (n_in % 128) != 0 || (n_out % 16) != 0 || bad_bits(bits);
 }
 
+// Every tensor is read or written in 16-byte pieces somewhere on the path.
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) != 0; }
+
 int common_checks(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
                   const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
                   void* workspace, size_t workspace_bytes, int64_t need) {
     if (m < 0 || bad_shape(n_in, n_out, bits)) return EXL3_EINVAL;
     if (m == 0) return EXL3_OK;
     if (!x || !trellis || !sign || !out_scale || !y) return EXL3_EINVAL;
+    if (misaligned(x) || misaligned(trellis) || misaligned(sign) || misaligned(out_scale) || misaligned(y) ||
+        misaligned(workspace))
+        return EXL3_EINVAL;
     if ((const void*)x == (const void*)y) return EXL3_EINVAL;
     if (need > 0 && (!workspace || (int64_t)workspace_bytes < need)) return EXL3_EWORKSPACE;
     // weights are read through 32-bit buffer offsets
@@ -214,6 +220,7 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles, uint1
     if (bad_bits(bits) || n_tiles < 0) return EXL3_EINVAL;
     if (n_tiles == 0) return EXL3_OK;
     if (!words || !out) return EXL3_EINVAL;
+    if (misaligned(words) || misaligned(out)) return EXL3_EINVAL;
     if (n_tiles > (int64_t)0xFFFFFFFF * 16) return EXL3_EUNSUPPORTED;
     hipError_t e = exl3::launch_decode(k_of(bits), cb_of(bits), words, n_tiles, out, (hipStream_t)stream);
     return e == hipSuccess ? EXL3_OK : EXL3_EHIP;
@@ -230,10 +237,12 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
     }
     if (m == 0) return EXL3_OK;
     if (!x || !sign) return EXL3_EINVAL;
+    if (misaligned(x) || misaligned(sign) || misaligned(workspace)) return EXL3_EINVAL;
     int64_t strips = 0;
     for (int i = 0; i < n_proj; ++i) {
         const exl3_proj_t& q = proj[i];
         if (!q.trellis || !q.out_scale || !q.y) return EXL3_EINVAL;
+        if (misaligned(q.trellis) || misaligned(q.out_scale) || misaligned(q.y)) return EXL3_EINVAL;
         if ((const void*)q.y == (const void*)x) return EXL3_EINVAL;
         for (int j = 0; j < i; ++j)
             if (proj[j].y == q.y) return EXL3_EINVAL;
@@ -362,6 +371,7 @@ int exl3_encode_tiles(const float* w, int64_t n_tiles, int32_t bits, uint16_t* w
     if (bad_bits(bits) || n_tiles < 0) return EXL3_EINVAL;
     if (n_tiles == 0) return EXL3_OK;
     if (!w || !words) return EXL3_EINVAL;
+    if (misaligned(w) || misaligned(words) || misaligned(costs) || misaligned(workspace)) return EXL3_EINVAL;
     const int64_t slot = exl3::encode_slot_bytes(k_of(bits));
     if (!workspace || (int64_t)workspace_bytes < slot) return EXL3_EWORKSPACE;
     int64_t slots = (int64_t)workspace_bytes / slot;

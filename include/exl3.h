@@ -32,8 +32,9 @@
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers owned by the caller; the library allocates
- *     nothing and keeps no per-call state.  Tensors are contiguous, row-major,
- *     and at least 16-byte aligned.  x and y must not alias.
+ *     nothing and keeps no per-call state.  Tensors (and workspaces) are
+ *     contiguous, row-major, and at least 16-byte aligned: a call given a
+ *     misaligned pointer returns EXL3_EINVAL.  x and y must not alias.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     asynchronous: argument errors are returned synchronously, before any
  *     launch; launch failures are reported as EXL3_EHIP from hipGetLastError

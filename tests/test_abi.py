@@ -80,7 +80,8 @@ def test_status_strings(lib):
     assert ex.status_string(-3).startswith("workspace")
 
 
-def _gemv_call(lib, fn, x=1, m=1, tr=1, sg=1, sc=1, n_in=128, n_out=16, bits=4, y=2, ws=3, wsb=1 << 30):
+def _gemv_call(lib, fn, x=0x1000, m=1, tr=0x2000, sg=0x3000, sc=0x4000, n_in=128, n_out=16, bits=4, y=0x5000,
+               ws=0x6000, wsb=1 << 30):
     return getattr(lib, fn)(x, m, tr, sg, sc, n_in, n_out, bits, y, ws, wsb, None)
 
 
@@ -97,7 +98,9 @@ def test_linear_argument_errors_return_before_launch(lib, fn):
     assert _gemv_call(lib, fn, sg=None) == -1
     assert _gemv_call(lib, fn, sc=None) == -1
     assert _gemv_call(lib, fn, y=None) == -1
-    assert _gemv_call(lib, fn, x=5, y=5) == -1          # aliasing
+    assert _gemv_call(lib, fn, x=0x5000, y=0x5000) == -1  # aliasing
+    for arg in ("x", "tr", "sg", "sc", "y", "ws"):  # every pointer 16-byte aligned
+        assert _gemv_call(lib, fn, **{arg: 0x7008}) == -1, arg
     assert _gemv_call(lib, fn, m=0, x=None, y=None) == 0  # m == 0 is a no-op
     # weights of 2 GiB or more are refused (32-bit buffer offsets)
     assert _gemv_call(lib, fn, n_in=65536, n_out=65536, bits=4) == -2
@@ -123,15 +126,15 @@ def test_gemv_rejects_m_above_16(lib):
     assert _gemv_call(lib, "exl3_gemv", m=17) == -1
 
 
-def _multi_call(lib, projs, x=1, m=1, sg=1, n_in=128, bits=4, n_proj=None):
+def _multi_call(lib, projs, x=0x1000, m=1, sg=0x1010, n_in=128, bits=4, n_proj=None, ws=None):
     arr = (ex._Proj * max(len(projs), 1))(*[ex._Proj(*p_) for p_ in projs])
     return lib.exl3_gemv_multi(x, m, sg, n_in, bits, arr if projs else None,
-                               len(projs) if n_proj is None else n_proj, None, 0, None)
+                               len(projs) if n_proj is None else n_proj, ws, 0, None)
 
 
 def test_gemv_multi_argument_errors(lib):
     # (trellis, out_scale, y, n_out, reserved); fake pointers, never dereferenced
-    good = [(11, 12, 13, 16, 0), (21, 22, 23, 32, 0)]
+    good = [(0x110, 0x120, 0x130, 16, 0), (0x210, 0x220, 0x230, 32, 0)]
     assert _multi_call(lib, good, m=-1) == -1
     assert _multi_call(lib, good, m=17) == -1
     assert _multi_call(lib, good, n_in=100) == -1
@@ -142,15 +145,21 @@ def test_gemv_multi_argument_errors(lib):
     assert _multi_call(lib, good * 3) == -1                       # 6 > EXL3_GEMV_MAX_PROJ
     assert _multi_call(lib, good, x=None) == -1
     assert _multi_call(lib, good, sg=None) == -1
-    assert _multi_call(lib, [(0, 12, 13, 16, 0)]) == -1
-    assert _multi_call(lib, [(11, 0, 13, 16, 0)]) == -1
-    assert _multi_call(lib, [(11, 12, 0, 16, 0)]) == -1
-    assert _multi_call(lib, [(11, 12, 13, 24, 0)]) == -1          # n_out % 16
-    assert _multi_call(lib, [(11, 12, 13, 0, 0)]) == -1
-    assert _multi_call(lib, [(11, 12, 1, 16, 0)]) == -1           # y aliases x
-    assert _multi_call(lib, [(11, 12, 13, 16, 0), (21, 22, 13, 16, 0)]) == -1  # same y twice
-    assert _multi_call(lib, good, m=0, x=None, sg=None) == 0     # m == 0 is a no-op
-    assert _multi_call(lib, [(11, 12, 13, 65536, 0)], n_in=65536) == -2  # >= 2 GiB of weights
+    assert _multi_call(lib, [(0, 0x120, 0x130, 16, 0)]) == -1
+    assert _multi_call(lib, [(0x110, 0, 0x130, 16, 0)]) == -1
+    assert _multi_call(lib, [(0x110, 0x120, 0, 16, 0)]) == -1
+    assert _multi_call(lib, [(0x110, 0x120, 0x130, 24, 0)]) == -1          # n_out % 16
+    assert _multi_call(lib, [(0x110, 0x120, 0x130, 0, 0)]) == -1
+    assert _multi_call(lib, [(0x110, 0x120, 0x1000, 16, 0)]) == -1         # y aliases x
+    assert _multi_call(lib, [(0x110, 0x120, 0x130, 16, 0), (0x210, 0x220, 0x130, 16, 0)]) == -1  # same y twice
+    assert _multi_call(lib, good, m=0, x=None, sg=None) == 0              # m == 0 is a no-op
+    assert _multi_call(lib, [(0x110, 0x120, 0x130, 65536, 0)], n_in=65536) == -2  # >= 2 GiB of weights
+    # every pointer 16-byte aligned
+    assert _multi_call(lib, good, x=0x1008) == -1
+    assert _multi_call(lib, good, sg=0x1018) == -1
+    assert _multi_call(lib, good, ws=0x2004) == -1
+    for bad in ((0x118, 0x120, 0x130, 16, 0), (0x110, 0x122, 0x130, 16, 0), (0x110, 0x120, 0x131, 16, 0)):
+        assert _multi_call(lib, [bad]) == -1
 
 
 def test_encode_sizes_and_argument_errors(lib):
@@ -159,22 +168,28 @@ def test_encode_sizes_and_argument_errors(lib):
         assert lib.exl3_encode_slot_bytes(K | ex.CODEBOOK_BYTE_SUM) == 256 * (1 << (16 - K))
     assert lib.exl3_encode_slot_bytes(0) == -1 and lib.exl3_encode_slot_bytes(9) == -1
     big = 1 << 30
-    assert lib.exl3_encode_tiles(1, 1, 0, 2, None, 3, big, None) == -1       # bad bits
-    assert lib.exl3_encode_tiles(1, -1, 4, 2, None, 3, big, None) == -1      # n_tiles < 0
-    assert lib.exl3_encode_tiles(None, 1, 4, 2, None, 3, big, None) == -1
-    assert lib.exl3_encode_tiles(1, 1, 4, None, None, 3, big, None) == -1
-    assert lib.exl3_encode_tiles(1, 1, 4, 2, None, None, big, None) == -3    # no workspace
-    assert lib.exl3_encode_tiles(1, 1, 4, 2, None, 3, 1000, None) == -3      # below one slot
-    assert lib.exl3_encode_tiles(None, 0, 4, None, None, None, 0, None) == 0  # no tiles: no-op
+    w, words, ws = 0x1000, 0x2000, 0x3000  # fake pointers, never dereferenced
+    assert lib.exl3_encode_tiles(w, 1, 0, words, None, ws, big, None) == -1       # bad bits
+    assert lib.exl3_encode_tiles(w, -1, 4, words, None, ws, big, None) == -1      # n_tiles < 0
+    assert lib.exl3_encode_tiles(None, 1, 4, words, None, ws, big, None) == -1
+    assert lib.exl3_encode_tiles(w, 1, 4, None, None, ws, big, None) == -1
+    assert lib.exl3_encode_tiles(w, 1, 4, words, None, None, big, None) == -3    # no workspace
+    assert lib.exl3_encode_tiles(w, 1, 4, words, None, ws, 1000, None) == -3     # below one slot
+    assert lib.exl3_encode_tiles(None, 0, 4, None, None, None, 0, None) == 0     # no tiles: no-op
+    for args in ((w + 4, words, None, ws), (w, words + 2, None, ws), (w, words, 0x4004, ws), (w, words, None, ws + 8)):
+        assert lib.exl3_encode_tiles(args[0], 1, 4, args[1], args[2], args[3], big, None) == -1  # misaligned
 
 
 def test_decode_tile_argument_errors(lib):
-    assert lib.exl3_decode_tile(1, 0, 1, 2, None) == -1
-    assert lib.exl3_decode_tile(1, 9, 1, 2, None) == -1
-    assert lib.exl3_decode_tile(1, 4, -1, 2, None) == -1
-    assert lib.exl3_decode_tile(None, 4, 1, 2, None) == -1
-    assert lib.exl3_decode_tile(1, 4, 1, None, None) == -1
+    words, out = 0x1000, 0x2000  # fake pointers, never dereferenced
+    assert lib.exl3_decode_tile(words, 0, 1, out, None) == -1
+    assert lib.exl3_decode_tile(words, 9, 1, out, None) == -1
+    assert lib.exl3_decode_tile(words, 4, -1, out, None) == -1
+    assert lib.exl3_decode_tile(None, 4, 1, out, None) == -1
+    assert lib.exl3_decode_tile(words, 4, 1, None, None) == -1
     assert lib.exl3_decode_tile(None, 4, 0, None, None) == 0
+    assert lib.exl3_decode_tile(words + 2, 4, 1, out, None) == -1  # misaligned
+    assert lib.exl3_decode_tile(words, 4, 1, out + 8, None) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
