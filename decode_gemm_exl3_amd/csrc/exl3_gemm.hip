@@ -256,6 +256,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
 // wave per SIMD nothing else covers a stall.  One barrier per step.
 // ---------------------------------------------------------------------------
 constexpr int G4_BUFS = 4;  // x' buffers in LDS, 32 KB each: [group 8][row 256] x 16 bytes
+constexpr int G4_TLD = 72;  // halves per row of a wave's 256 x 64 output tile in LDS (144 bytes: rows of a
+                            // 16-byte read stay aligned, rows 4 apart fall on different banks)
+constexpr int G4_LDS = (G4_BUFS * 8 * 256 * 16 > 4 * GEMM_BM * G4_TLD * 2) ? G4_BUFS * 8 * 256 * 16
+                                                                            : 4 * GEMM_BM * G4_TLD * 2;
 
 #define G4_FENCE __builtin_amdgcn_sched_barrier(0)
 
@@ -320,7 +324,7 @@ __device__ __forceinline__ void g4_mfma(f32x4_t& d, const half8_t& a, const u32x
 
 template <int K, int CB>
 __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
-    __shared__ __align__(16) u32x4_t As[G4_BUFS * 8 * 256];
+    __shared__ __align__(16) u32x4_t As[G4_LDS / 16];  // x' staging, then the output tiles
     constexpr int NB = RowGeom<K>::NB;
     constexpr uint32_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
     const int tid = threadIdx.x;
@@ -488,18 +492,48 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
         }
         return;
     }
+    // y through LDS: each wave puts its 256 x 64 fp16 tile in LDS row by row and
+    // writes it out in 16-byte runs of rows (eight outputs), not in 2-byte
+    // pieces.  The staging loads of the last steps (past the end) still land
+    // in LDS, so every one has to finish first.
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0)
+    __syncthreads();
+    uint16_t* T = reinterpret_cast<uint16_t*>(As) + wave * (GEMM_BM * G4_TLD);
+    float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int o = (s0 + j) * 16 + n;
-        if (o >= p.n_out) continue;
-        const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
+        sc[j] = o < p.n_out ? __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f : 0.0f;
+    }
+    // lanes n and n ^ 1 hold the same four rows of neighbouring outputs: the
+    // even lane writes rows 0 and 1 of the pair of outputs, the odd lane rows
+    // 2 and 3, each as fp16 pairs, after trading two values across the pair
+    const bool odd = (n & 1) != 0;
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    auto pk = [](float a, float b) { return __builtin_bit_cast(uint32_t, h2_t{(_Float16)a, (_Float16)b}); };
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 16; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + i * 16 + 4 * g + r;
-                if (row < p.m) p.y[(int64_t)row * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * acc[i][j][r]));
-            }
+        for (int j = 0; j < 4; ++j) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = sc[j] * acc[i][j][r];
+            const float x0 = odd ? v[0] : v[2], x1 = odd ? v[1] : v[3];
+            // quad_perm [1, 0, 3, 2]: the value of lane n ^ 1
+            const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x0), 0xB1, 0xF, 0xF, false));
+            const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x1), 0xB1, 0xF, 0xF, false));
+            const int row = 16 * i + 4 * g + (odd ? 2 : 0);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(T + row * G4_TLD + 16 * j + (n & ~1));
+            dst[0] = odd ? pk(t0, v[2]) : pk(v[0], t0);
+            dst[G4_TLD / 2] = odd ? pk(t1, v[3]) : pk(v[1], t1);
+        }
+    // a wave reads back only its own tile, and its LDS operations run in order
+#pragma unroll 4
+    for (int t = 0; t < GEMM_BM * 8 / 64; ++t) {
+        const int c = lane + 64 * t, row = c >> 3, part = c & 7;  // 8 runs of 8 outputs per row
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(T + row * G4_TLD + part * 8);
+        const int grow = m0 + row, o = 16 * s0 + 8 * part;
+        if (grow < p.m && o < p.n_out) *reinterpret_cast<u32x4_t*>(p.y + (int64_t)grow * p.n_out + o) = v;
     }
 }
 #undef G4_FENCE
