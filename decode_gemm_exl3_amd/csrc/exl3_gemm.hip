@@ -258,8 +258,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
 constexpr int G4_BUFS = 4;  // x' buffers in LDS, 32 KB each: [group 8][row 256] x 16 bytes
 constexpr int G4_TLD = 72;  // halves per row of a wave's 256 x 64 output tile in LDS (144 bytes: rows of a
                             // 16-byte read stay aligned, rows 4 apart fall on different banks)
+constexpr int G4_TLDF = 68;  // floats per row of a wave's 128 x 64 fp32 half tile (272 bytes, same reasons)
 constexpr int G4_LDS = (G4_BUFS * 8 * 256 * 16 > 4 * GEMM_BM * G4_TLD * 2) ? G4_BUFS * 8 * 256 * 16
                                                                             : 4 * GEMM_BM * G4_TLD * 2;
+static_assert(4 * (GEMM_BM / 2) * G4_TLDF * 4 <= G4_LDS, "fp32 half tiles fit the LDS of the kernel");
 
 #define G4_FENCE __builtin_amdgcn_sched_barrier(0)
 
@@ -475,29 +477,36 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
     // the last MFMAs' results: 8-pass writes need 11 wait states before a read
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
 
-    // D[4g + r][n] of (rt, j): row m0 + 16 rt + 4g + r, output 16 (s0 + j) + n
-    if (p.zsplit > 1) {
+    // D[4g + r][n] of (rt, j): row m0 + 16 rt + 4g + r, output 16 (s0 + j) + n.
+    // The results leave through LDS, each wave's tile row by row, in 16-byte
+    // runs of rows rather than 2- or 4-byte pieces.  The staging loads of the
+    // last steps (past the end) still land in LDS, so every one has to finish
+    // first; afterwards a wave reads back only its own tile, and its LDS
+    // operations run in order.
+    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0)
+    __syncthreads();
+    if (p.zsplit > 1) {  // fp32 partial sums of this split, 128 rows of the tile at a time
         float* part = p.part + (int64_t)blockIdx.z * p.m * p.n_out;
+        float* T = reinterpret_cast<float*>(As) + wave * (GEMM_BM / 2) * G4_TLDF;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int o = (s0 + j) * 16 + n;
-            if (o >= p.n_out) continue;
+        for (int hb = 0; hb < 2; ++hb) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + i * 16 + 4 * g + r;
-                    if (row < p.m) part[(int64_t)row * p.n_out + o] = acc[i][j][r];
-                }
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) T[(16 * i + 4 * g + r) * G4_TLDF + 16 * j + n] = acc[8 * hb + i][j][r];
+#pragma unroll 4
+            for (int t = 0; t < (GEMM_BM / 2) * 16 / 64; ++t) {
+                const int c = lane + 64 * t, row = c >> 4, q = c & 15;  // 16 runs of 4 outputs per row
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(T + row * G4_TLDF + q * 4);
+                const int grow = m0 + 128 * hb + row, o = 16 * s0 + 4 * q;
+                if (grow < p.m && o < p.n_out) *reinterpret_cast<u32x4_t*>(part + (int64_t)grow * p.n_out + o) = v;
+            }
         }
         return;
     }
-    // y through LDS: each wave puts its 256 x 64 fp16 tile in LDS row by row and
-    // writes it out in 16-byte runs of rows (eight outputs), not in 2-byte
-    // pieces.  The staging loads of the last steps (past the end) still land
-    // in LDS, so every one has to finish first.
-    __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);  // vmcnt(0)
-    __syncthreads();
+    // y: fp16, eight outputs per 16-byte run
     uint16_t* T = reinterpret_cast<uint16_t*>(As) + wave * (GEMM_BM * G4_TLD);
     float sc[4];
 #pragma unroll
