@@ -34,6 +34,20 @@ constexpr int GM_BN = GEMM_BN;        // 16 strips, 64 outputs per wave
 constexpr int GM_BK = 64;             // 4 tile columns
 constexpr int GM_LD = GM_BK + 8;      // padded LDS row stride in halves (144 bytes)
 constexpr int GM_B_FRAGS = 2 * 4 * 4 * 64;  // [k half][output quarter][fragment][lane], 16 bytes each
+constexpr int GM_TLD = 72;   // halves per row of a wave's 16 x 64 fp16 output fragment in LDS (144 bytes)
+constexpr int GM_TLDF = 68;  // floats per row of the same in fp32 (272 bytes)
+static_assert(8 * 16 * GM_TLDF * 4 <= 2 * GM_B_FRAGS * 16, "output fragments of 8 waves fit the B buffers");
+
+// fp16 pair (RNE), first value in the low half.
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, h2_t{(_Float16)a, (_Float16)b});
+}
+
+// The value of lane n ^ 1 (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ float lane_pair_swap(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
 
 // BM = 64 rows per block for m <= 64, 128 for m <= 128 (the decode of each
 // weight is most of the work at such m, and larger blocks would multiply
@@ -192,35 +206,61 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
         main_loop(std::integral_constant<int, 0>{});
     else
         main_loop(std::integral_constant<int, 1>{});
-    // D[4g + r][n] of fragment (i, j): row WR mh + 16i + 4g + r, output 16 (s0 + j) + n
+    // D[4g + r][n] of fragment (i, j): row WR mh + 16i + 4g + r, output 16 (s0 + j) + n.
+    // The results leave through LDS (the B buffers, free after the last
+    // barrier), one 16-row fragment at a time in a region of each wave's own,
+    // in 16-byte runs of rows rather than 2- or 4-byte pieces.  A wave reads
+    // back only what it wrote, and its LDS operations run in order.
     if (p.zsplit > 1) {  // fp32 partial sums of this split; the reduction scales them
         float* part = p.part + (int64_t)blockIdx.z * p.m * p.n_out;
+        float* T = reinterpret_cast<float*>(&Bs[0][0]) + wave * 16 * GM_TLDF;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int o = (s0 + j) * 16 + n;
-            if (o >= p.n_out) continue;
+        for (int i = 0; i < RF; ++i) {
 #pragma unroll
-            for (int i = 0; i < RF; ++i)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + WR * mh + i * 16 + 4 * g + r;
-                    if (row < p.m) part[(int64_t)row * p.n_out + o] = acc[i][j][r];
-                }
+                for (int r = 0; r < 4; ++r) T[(4 * g + r) * GM_TLDF + 16 * j + n] = acc[i][j][r];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int c = lane + 64 * t, row = c >> 4, q = c & 15;  // 16 runs of 4 outputs per row
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(T + row * GM_TLDF + q * 4);
+                const int grow = m0 + WR * mh + 16 * i + row, o = 16 * s0 + 4 * q;
+                if (grow < p.m && o < p.n_out) *reinterpret_cast<u32x4_t*>(part + (int64_t)grow * p.n_out + o) = v;
+            }
         }
         return;
     }
+    uint16_t* T = reinterpret_cast<uint16_t*>(&Bs[0][0]) + wave * 16 * GM_TLD;
+    float sc[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int o = (s0 + j) * 16 + n;
-        if (o >= p.n_out) continue;
-        const float sc = __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f;
+        sc[j] = o < p.n_out ? __half2float(__ushort_as_half(p.out_scale[o])) * 128.0f : 0.0f;
+    }
+    // lanes n and n ^ 1 hold the same four rows of neighbouring outputs: the
+    // even lane writes rows 0 and 1 of the pair of outputs, the odd lane rows
+    // 2 and 3, each as fp16 pairs, after trading two values across the pair
+    const bool odd = (n & 1) != 0;
 #pragma unroll
-        for (int i = 0; i < RF; ++i)
+    for (int i = 0; i < RF; ++i) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + WR * mh + i * 16 + 4 * g + r;
-                if (row < p.m) p.y[(int64_t)row * p.n_out + o] = __half_as_ushort(__float2half_rn(sc * acc[i][j][r]));
-            }
+        for (int j = 0; j < 4; ++j) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = sc[j] * acc[i][j][r];
+            const float x0 = odd ? v[0] : v[2], x1 = odd ? v[1] : v[3];
+            const float t0 = lane_pair_swap(x0), t1 = lane_pair_swap(x1);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(T + (4 * g + (odd ? 2 : 0)) * GM_TLD + 16 * j + (n & ~1));
+            dst[0] = odd ? pack_h2(t0, v[2]) : pack_h2(v[0], t0);
+            dst[GM_TLD / 2] = odd ? pack_h2(t1, v[3]) : pack_h2(v[1], t1);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int c = lane + 64 * t, row = c >> 3, q = c & 7;  // 8 runs of 8 outputs per row
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(T + row * GM_TLD + q * 8);
+            const int grow = m0 + WR * mh + 16 * i + row, o = 16 * s0 + 8 * q;
+            if (grow < p.m && o < p.n_out) *reinterpret_cast<u32x4_t*>(p.y + (int64_t)grow * p.n_out + o) = v;
+        }
     }
 }
 
@@ -518,8 +558,6 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
     // even lane writes rows 0 and 1 of the pair of outputs, the odd lane rows
     // 2 and 3, each as fp16 pairs, after trading two values across the pair
     const bool odd = (n & 1) != 0;
-    typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-    auto pk = [](float a, float b) { return __builtin_bit_cast(uint32_t, h2_t{(_Float16)a, (_Float16)b}); };
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -528,13 +566,11 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = sc[j] * acc[i][j][r];
             const float x0 = odd ? v[0] : v[2], x1 = odd ? v[1] : v[3];
-            // quad_perm [1, 0, 3, 2]: the value of lane n ^ 1
-            const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x0), 0xB1, 0xF, 0xF, false));
-            const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x1), 0xB1, 0xF, 0xF, false));
+            const float t0 = lane_pair_swap(x0), t1 = lane_pair_swap(x1);
             const int row = 16 * i + 4 * g + (odd ? 2 : 0);
             uint32_t* dst = reinterpret_cast<uint32_t*>(T + row * G4_TLD + 16 * j + (n & ~1));
-            dst[0] = odd ? pk(t0, v[2]) : pk(v[0], t0);
-            dst[G4_TLD / 2] = odd ? pk(t1, v[3]) : pk(v[1], t1);
+            dst[0] = odd ? pack_h2(t0, v[2]) : pack_h2(v[0], t0);
+            dst[G4_TLD / 2] = odd ? pack_h2(t1, v[3]) : pack_h2(v[1], t1);
         }
     // a wave reads back only its own tile, and its LDS operations run in order
 #pragma unroll 4
