@@ -121,6 +121,8 @@ def _need(t, name: str, dtypes, numel: int | None = None, shape=None) -> None:
         raise Exl3Error(f"{name}: {t.numel()} elements, expected {numel}")
     if not t.is_contiguous():
         raise Exl3Error(f"{name}: must be contiguous")
+    if t.numel() > 0 and t.data_ptr() % 16 != 0:
+        raise Exl3Error(f"{name}: data must be 16-byte aligned (a view at an offset is not)")
 
 
 def _on_gpu(**tensors) -> None:

@@ -1,6 +1,6 @@
 """The Python binding checks the tensors it hands to the library (element
-type, shape, element count, contiguity, device) and raises before anything is
-launched.  CPU only: every case fails before a device is touched."""
+type, shape, element count, contiguity, 16-byte alignment, device) and raises
+before anything is launched.  CPU only: every case fails before a device is touched."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,10 @@ def test_linear_rejects_bad_tensors(fn):
         f(x, tr, sign, sc, 3, y=y[:1])
     with pytest.raises(ex.Exl3Error, match="x: must be contiguous"):
         f(torch.zeros((256, 2), dtype=torch.float16).t(), tr, sign, sc, 3, y=y)
+    with pytest.raises(ex.Exl3Error, match="x: data must be 16-byte aligned"):
+        f(torch.zeros(2 * 256 + 1, dtype=torch.float16)[1:].view(2, 256), tr, sign, sc, 3, y=y)
+    with pytest.raises(ex.Exl3Error, match="y: data must be 16-byte aligned"):
+        f(x, tr, sign, sc, 3, y=torch.empty(2 * 32 + 4, dtype=torch.float16)[4:].view(2, 32))
     with pytest.raises(ex.Exl3Error, match="must be on a GPU device"):
         f(x, tr, sign, sc, 3, y=y)
 
