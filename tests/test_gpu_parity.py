@@ -424,6 +424,23 @@ def test_gemm_256_row_blocks(torch_cuda, K):
             assert np.array_equal(y.view(np.uint16), y2.view(np.uint16))
 
 
+def test_gemm_seeded_random_shapes(torch_cuda):
+    # shapes drawn once from a fixed seed across both GEMM kernels, bits,
+    # codebooks, ragged m and output counts, split and unsplit inputs
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        K = int(rng.integers(1, 9))
+        cb = int(rng.integers(0, 2))
+        n_in = 128 * int(rng.integers(1, 13))
+        n_out = 16 * int(rng.integers(1, 130))
+        m = int(rng.choice([int(rng.integers(1, 129)), int(rng.integers(129, 700))]))
+        log(f"gemm random case {case}: K={K} cb={cb} n_in={n_in} n_out={n_out} m={m}")
+        words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [43, case])
+        y = run_linear(torch_cuda, "gemm", words, x, sign, scale, K, cb=cb)
+        err = rel_fro(y, O.linear(x, words, sign, scale, K, cb=cb))
+        assert err <= TOL, (K, cb, n_in, n_out, m, err)
+
+
 def test_linear_dispatch(torch_cuda):
     # the measured table: GEMV for small m * n_in, the split GEMM beyond
     for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12)]:
