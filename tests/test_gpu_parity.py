@@ -441,6 +441,29 @@ def test_gemm_seeded_random_shapes(torch_cuda):
         assert err <= TOL, (K, cb, n_in, n_out, m, err)
 
 
+def test_gemv_seeded_random_shapes(torch_cuda):
+    # fused launches of 1..4 projections drawn from a fixed seed: bits,
+    # codebooks, m up to 16, input lengths up to 40 blocks (several LDS chunks
+    # at larger m), output counts that leave workgroups unevenly loaded
+    import decode_gemm_exl3_amd as ex
+    rng = np.random.default_rng(2025)
+    for case in range(16):
+        K = int(rng.integers(1, 9))
+        cb = int(rng.integers(0, 2))
+        n_in = 128 * int(rng.integers(1, 41))
+        m = int(rng.integers(1, 17))
+        n_outs = tuple(16 * int(rng.integers(1, 200)) for _ in range(int(rng.integers(1, 5))))
+        log(f"gemv random case {case}: K={K} cb={cb} n_in={n_in} n_outs={n_outs} m={m}")
+        words, x, sign, scales = group_case(n_in, n_outs, K, m, 600 + case)
+        ys = ex.gemv_multi(to_dev(torch_cuda, x), [(to_dev(torch_cuda, w), to_dev(torch_cuda, sc))
+                                                     for w, sc in zip(words, scales)], to_dev(torch_cuda, sign), K,
+                           codebook=cb)
+        torch_cuda.cuda.synchronize()
+        for w, sc, y in zip(words, scales, ys):
+            err = rel_fro(y.cpu().numpy(), O.linear(x, w, sign, sc, K, cb=cb))
+            assert err <= TOL, (K, cb, n_in, n_outs, m, err)
+
+
 def test_linear_dispatch(torch_cuda):
     # the measured table: GEMV for small m * n_in, the split GEMM beyond
     for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12)]:
