@@ -287,18 +287,77 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                    (uint32_t)(bytes - STEP_B)};
     };
 
-    // ---- weight stream first --------------------------------------------------
+    // Per-projection values for a lane's own projection index, picked with
+    // selects from scalar registers: an indexed read of the argument block is a
+    // vector load, and its wait would also cover the weight loads in flight.
+    // The empty asm keeps the compiler from folding the selects back into one.
+    static_assert(GEMV_MAX_PROJ == 4, "the selects below name every projection");
+    auto sel4 = [](int pi, auto a0, auto a1, auto a2, auto a3) {
+        asm volatile("" : "+s"(a0), "+s"(a1), "+s"(a2), "+s"(a3));
+        return pi == 0 ? a0 : pi == 1 ? a1 : pi == 2 ? a2 : a3;
+    };
+    auto scale_of = [&](int pi) {
+        return sel4(pi, p.out_scale[0], p.out_scale[1], p.out_scale[2], p.out_scale[3]);
+    };
+    auto y_of = [&](int pi) { return sel4(pi, p.y[0], p.y[1], p.y[2], p.y[3]); };
+    auto n_out_of = [&](int pi) { return sel4(pi, p.n_out[0], p.n_out[1], p.n_out[2], p.n_out[3]); };
+    auto begin_of = [&](int pi) { return sel4(pi, 0, p.strip_end[0], p.strip_end[1], p.strip_end[2]); };
+    const RowFwht fk = row_fwht_consts(lane & 15);
+    // 16 lanes per 128-input block, 8 inputs per lane (one 16-byte load of x
+    // and of sign): rotate block blk of a chunk of nblk blocks (row blk / nblk)
+    // into the chunk's LDS rows, xs[r][k] = dup(fp16(x'/128))
+    auto rotate_block = [&](int blk, int nblk, const u32x4_t& xv, const u32x4_t& sv) {
+        const int r = blk / nblk, bb = blk % nblk;
+        float v[8];
+        row_load_pairs(xv, sv, v);
+        fwht128_row(v, fk);
+        uint32_t d[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float t = v[e] * fk.osc;
+            d[e] = pack_half2(t, t);  // duplicated for the two codebook halves
+        }
+        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + bb * 128 + fk.pos * 8);
+        dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
+        dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+    };
+    auto block_col = [&](int blk, int nblk, int tc0) { return tc0 * 16 + (blk % nblk) * 128 + (lane & 15) * 8; };
+
+    // ---- first loads: x and sign of this thread's first rotation block, the
+    // weight stream, the scale of its first output in the final write.  The
+    // first block is rotated in straight-line code, so that its wait covers
+    // only the x and sign loads and the rotation runs under the weight burst;
+    // the scale's latency hides behind the whole stream.
+    const int nblk0 = (min(p.kc, p.tiles_in) * 16) >> 7;  // 128-input blocks of chunk 0
+    const bool xpre = !p.xr && (tid >> 4) < M * nblk0;
+    u32x4_t xv0{}, sv0{};
+    if (xpre) {
+        const int blk = tid >> 4, col = block_col(blk, nblk0, 0);
+        xv0 = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(blk / nblk0) * p.n_in + col);
+        sv0 = *reinterpret_cast<const u32x4_t*>(p.sign + col);
+    }
     uint32_t buf[PF][RowGeom<K>::NB];
     {
         const Seg s0 = seg_at(0, 0);
 #pragma unroll
         for (int u = 0; u < PF; ++u) load_row<K>(s0.rs, loff, min(s0.off + u * STEP_B, s0.lim), buf[u]);
     }
+    // Loaded by every thread (those past the last output re-read output 0, so
+    // the count of loads in flight does not depend on the thread), from global
+    // memory (a flat load would make the next wait cover every load), and
+    // converted where it is used, so that nothing waits for it here.
+    uint16_t sc0;
+    {
+        const int t = tid < nj * M * 16 ? tid : 0;
+        const int s = b + (t / (M * 16)) * G, pi = proj_of(s);
+        using gu16 = const __attribute__((address_space(1))) uint16_t*;
+        sc0 = *(gu16)(scale_of(pi) + (s - begin_of(pi)) * 16 + (t & 15));
+    }
+    if (xpre) rotate_block(tid >> 4, nblk0, xv0, sv0);
     for (int i = tid; i < PF * 64; i += 64 * W) zero[i] = 0u;
 
     const bool adata = n < M;
     const CbRegs cr = cb_regs<CB>();
-    const RowFwht fk = row_fwht_consts(lane & 15);
     for (int c = 0; c < p.n_kchunks; ++c) {
         const int tc0 = c * p.kc;
         const int kcount = min(p.kc, p.tiles_in - tc0);
@@ -325,25 +384,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
                     dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
                 }
         } else {
-            // 16 lanes per 128-input block, 8 inputs per lane (one 16-byte load)
+            // chunk 0's first block of each thread was rotated at the start
             const int nblk = (kcount * 16) >> 7;
-            for (int blk = tid >> 4; blk < M * nblk; blk += 4 * W) {
-                const int r = blk / nblk, bb = blk % nblk;
-                const int col = tc0 * 16 + bb * 128 + (lane & 15) * 8;
-                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)r * p.n_in + col);
+            for (int blk = (tid >> 4) + (c == 0 ? 4 * W : 0); blk < M * nblk; blk += 4 * W) {
+                const int col = block_col(blk, nblk, tc0);
+                const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(blk / nblk) * p.n_in + col);
                 const u32x4_t sv = *reinterpret_cast<const u32x4_t*>(p.sign + col);
-                float v[8];
-                row_load_pairs(xv, sv, v);
-                fwht128_row(v, fk);
-                uint32_t d[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float t = v[e] * fk.osc;
-                    d[e] = pack_half2(t, t);  // duplicated for the two codebook halves
-                }
-                u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + bb * 128 + fk.pos * 8);
-                dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
-                dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+                rotate_block(blk, nblk, xv, sv);
             }
         }
         __syncthreads();
@@ -416,9 +463,9 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         float v = 0.f;
         for (int w = 0; w < W; ++w) v += red[((j * W + w) * M + r) * 16 + cc];
         const int s = b + j * G, pi = proj_of(s);
-        const int o = (s - proj_begin(pi)) * 16 + cc;
-        const float sc = __half2float(__ushort_as_half(p.out_scale[pi][o])) * 128.0f;
-        p.y[pi][(int64_t)r * p.n_out[pi] + o] = __half_as_ushort(__float2half_rn(sc * v));
+        const int o = (s - begin_of(pi)) * 16 + cc;
+        const float sc = __half2float(__ushort_as_half(idx == tid ? sc0 : scale_of(pi)[o])) * 128.0f;
+        y_of(pi)[(int64_t)r * n_out_of(pi) + o] = __half_as_ushort(__float2half_rn(sc * v));
     }
 }
 
