@@ -34,6 +34,15 @@ inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
 // Most rows exl3_linear hands to the GEMV.
 constexpr int GEMV_LINEAR_MAX_M = 12;
 
+// Largest rotated GEMM input: it is read through one buffer resource (at most
+// 2^31 - 16 bytes) with 32-bit offsets.
+constexpr int64_t GEMM_MAX_ROT_BYTES = ((int64_t)1 << 31) - ((int64_t)1 << 20);
+
+// exl3_linear's choice of path: the GEMV while m <= 12 and m * n_in <= 2^17.
+bool linear_uses_gemv(int32_t m, int32_t n_in) {
+    return m <= GEMV_LINEAR_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
+}
+
 // Input length from which a GEMV of 2..8 rows with enough workspace rotates its input in a pre-pass.
 constexpr int GEMV_PREROT_MIN_N_IN = 12288;
 
@@ -305,6 +314,8 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
                            gemm_rot_bytes(n_in, m > 0 ? m : 1));
     if (rc <= 0) return rc;
     if ((int64_t)m > (int64_t)65535 * 64) return EXL3_EUNSUPPORTED;
+    // the rotated input is read through one buffer resource with 32-bit offsets
+    if (gemm_rot_bytes(n_in, m) >= GEMM_MAX_ROT_BYTES) return EXL3_EUNSUPPORTED;
     uint16_t* xr = static_cast<uint16_t*>(workspace);
     // split the input dimension while the output blocks leave CUs idle, as far
     // as the workspace holds the partial sums (no split needs none)
@@ -356,7 +367,7 @@ int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uin
     // GEMV wins through m = 12 at n_in = 4096 and through m = 8 at n_in = 14336
     // (its x' of the m rows, 4 bytes per input, has to fit the LDS chunks), so
     // m <= 12 with m * n_in <= 2^17.
-    const bool use_gemv = m <= GEMV_LINEAR_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
+    const bool use_gemv = linear_uses_gemv(m, n_in);
     return use_gemv ? exl3_gemv(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream)
                     : exl3_gemm(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream);
 }

@@ -79,7 +79,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
 
     // ---- weights: fragment j = strip s0 + j, tile column 2 mh + (g >> 1) of the
     // step, half g & 1 of row n.  Lane offsets are fixed; strip and step go in
-    // the scalar offset.  Strips past the end read as zero (never written out).
+    // the scalar offset.  Both are clamped to the last strip and the last step,
+    // so no load leaves the weights: strips past the end re-read the last strip
+    // (their outputs are never written) and the prefetch past the last step
+    // re-reads it (its decode is never used).
     constexpr int KDH = HalfGeom<K>::KDH;
     constexpr uint32_t TILE_B = RowGeom<K>::DW_PER_TILE * 4;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.trellis, (int64_t)p.n_strips * p.tiles_in * TILE_B);
@@ -90,8 +93,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     const uint32_t bsh = half_shift<K>(n, h);
     const uint32_t strip_b = (uint32_t)p.tiles_in * TILE_B;
     uint32_t rows[4][KDH];  // the next step to decode
+    const int last_tc = p.tiles_in - 4;  // first tile column of the last step
     auto load_frag = [&](int j, int tc) {
-        const uint32_t so = (uint32_t)(s0 + j) * strip_b + (uint32_t)(tc + 2 * mh) * TILE_B;
+        const uint32_t so = (uint32_t)min(s0 + j, p.n_strips - 1) * strip_b + (uint32_t)(min(tc, last_tc) + 2 * mh) * TILE_B;
 #pragma unroll
         for (int i = 0; i < KDH; ++i) rows[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff[i], so, kNT);
     };
@@ -127,7 +131,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
     // ---- x' staging: each load instruction of a wave covers 8 whole rows of the
     // step (8 lanes x 16 bytes per row), so wave w stages rows (BM / 8) w ..
     // + BM / 8 - 1 in BM / 64 loads.  Rows past m read as zero through the
-    // buffer range check.
+    // buffer range check (the row is in the lane offset); the column goes in the
+    // scalar offset, clamped to the last step so that no load leaves its row.
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.xr + (int64_t)m0 * p.n_in, ((int64_t)p.m - m0) * p.n_in * 2);
     const int arow = (BM / 8) * wave + (lane >> 3), acol = (lane & 7) * 8;  // row of load c: arow + 8c; col in halves
     const uint32_t aoff = (uint32_t)arow * p.n_in * 2 + acol * 2;
@@ -137,7 +142,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int c = 0; c < AL; ++c)  // past the end: range check
             areg[c] = __builtin_bit_cast(u32x4_t,
-                                         __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + c * arow8, tc * 32, 0));
+                                         __builtin_amdgcn_raw_buffer_load_b128(ra, aoff + c * arow8,
+                                                                               min(tc, last_tc) * 32, 0));
     };
     auto store_a = [&](int buf) {
 #pragma unroll
@@ -384,20 +390,26 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
     const CbRegs cr = cb_regs<CB>();
 
     // weights: lane (n, g) loads row n of tile column 4 ks + g of strips s0 .. s0 + 3.
-    // Strips past the end and steps past the last read as zero or as other
-    // weights; neither reaches an output that is written.
+    // The strip and the step go in the scalar offset, clamped to the last strip
+    // and the last step, so no load leaves the weights: strips past the end
+    // re-read the last strip (their outputs are never written), steps past the
+    // last re-read it (their decode is never used).
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.trellis, (int64_t)p.n_strips * p.tiles_in * TILE_B);
     const uint32_t voff = (uint32_t)g * TILE_B + row_offset<K>(n);
     const uint32_t strip_b = (uint32_t)p.tiles_in * TILE_B;
     uint32_t rows[2][4][NB];  // [step parity][strip]
     uint32_t bq[2][4][4];     // B operands [k half][strip]
+    const int last_ks = p.tiles_in / 4 - 1;
     auto load_rows = [&](uint32_t (&rr)[4][NB], int j, int ks) {
-        load_row<K>(rs, voff, (uint32_t)(s0 + j) * strip_b + (uint32_t)ks * 4 * TILE_B, rr[j]);
+        load_row<K>(rs, voff, (uint32_t)min(s0 + j, p.n_strips - 1) * strip_b + (uint32_t)min(ks, last_ks) * 4 * TILE_B,
+                    rr[j]);
     };
 
     // x': wave w stages groups 2w and 2w + 1 of a step, 64 rows per load,
     // straight from memory into LDS (buffer loads to LDS: M0 holds the wave's
-    // destination, lane i writes 16 bytes at +16 i)
+    // destination, lane i writes 16 bytes at +16 i).  The group goes in the
+    // scalar offset, its step clamped to the last, so the staging past the last
+    // step re-reads it (into a buffer nothing reads) instead of leaving x'.
     const int64_t xrows = p.rows;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.xr, xrows * p.n_in * 2);
     const uint32_t avoff = (uint32_t)(m0 + lane) * 16;
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(256, 1) void gemm4_kernel(GemmParams p) {
         const int c = 2 * wave + (i >> 2), q = i & 3;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             ra, (__attribute__((address_space(3))) void*)(As + buf * 2048 + c * 256 + q * 64), 16,
-            avoff + (uint32_t)q * 1024, (uint32_t)(ks * 8 + c) * agrp, 0, 0);
+            avoff + (uint32_t)q * 1024, (uint32_t)(min(ks, last_ks) * 8 + c) * agrp, 0, 0);
     };
     // fragment (row tile rt, k half h) of a buffer: lane (n, g) reads group 2g + h of row 16 rt + n
     const int afrag = 2 * g * 256 + n;

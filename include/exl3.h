@@ -162,7 +162,10 @@ int exl3_gemv_multi(const uint16_t* x, int32_t m, const uint16_t* sign, int32_t 
  * across workgroups (few output blocks), fp32 partial sums: a workspace of the
  * size exl3_pack_info gives always suffices, a smaller one (at least
  * rows*n_in*2 bytes rounded up to 256, with rows = m for m <= 128 and m rounded
- * up to a multiple of 256 beyond) splits less.
+ * up to a multiple of 256 beyond) splits less.  EXL3_EUNSUPPORTED, before any
+ * launch, when the rotated input (rows*n_in*2 bytes) reaches 2^31 - 2^20 bytes
+ * (it is read through 32-bit offsets; e.g. n_in = 8192 at m > 130816) or
+ * m > 65535*64: split such a call into row blocks.
  */
 int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
               const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,

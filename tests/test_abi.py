@@ -29,7 +29,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemv_multi", "exl3_gemm",
-                          "exl3_linear", "exl3_encode_slot_bytes", "exl3_encode_tiles", "exl3_status_string"}
+                          "exl3_linear", "exl3_encode_slot_bytes", "exl3_encode_tiles",
+                          "exl3_status_string"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -197,3 +198,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ex, "_LIB", None)
     with pytest.raises(ex.Exl3Error):
         ex.load()
+
+
+def test_gemm_rejects_rotated_input_of_2_gib(lib):
+    # the rotated input is read through 32-bit offsets: 131072 rows of 8192
+    # inputs (2 GiB) is refused before any launch, with any workspace
+    A = 1 << 20
+    big = 1 << 40
+    assert lib.exl3_gemm(A, 131072, A, A, A, 8192, 16, 4, A + 64, A + 128, big, None) == -2
+    assert lib.exl3_linear(A, 131072, A, A, A, 8192, 16, 4, A + 64, A + 128, big, None) == -2
