@@ -20,7 +20,7 @@ import ctypes
 import os
 
 __all__ = ["Exl3Error", "lib_path", "load", "pack_info", "Workspace", "decode_tile", "gemv", "gemv_multi",
-           "gemm", "linear", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg", "encode_slot_bytes",
+           "gemm", "linear", "linear_noalloc", "status_string", "MAX_PROJ", "CODEBOOK_BYTE_SUM", "bits_arg", "encode_slot_bytes",
            "encode_tiles"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -69,6 +69,8 @@ def load() -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp, sz, vp]
         f.restype = ctypes.c_int
+    lib.exl3_linear_noalloc.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, vp, vp]
+    lib.exl3_linear_noalloc.restype = ctypes.c_int
     lib.exl3_gemv_multi.argtypes = [vp, i32, vp, i32, i32, ctypes.POINTER(_Proj), i32, vp, sz, vp]
     lib.exl3_gemv_multi.restype = ctypes.c_int
     lib.exl3_encode_slot_bytes.argtypes = [i32]
@@ -243,6 +245,18 @@ def gemv_multi(x, weights, sign, bits: int, ys=None, workspace=None, stream=None
 def linear(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):
     """Any m >= 1: the GEMV or the GEMM, as the library's measured table picks."""
     return _linear("exl3_linear", x, trellis, sign, out_scale, bits, workspace, y, stream, codebook)
+
+
+def linear_noalloc(x, trellis, sign, out_scale, bits: int, y, stream=None, codebook: int = 0):
+    """exl3_linear_noalloc: linear() into a caller-given y, with the library's
+    static per-GPU scratch instead of a workspace (nothing is allocated)."""
+    m, n_in = x.shape
+    n_out = out_scale.shape[0]
+    _check_linear(x, trellis, sign, out_scale, bits, y)
+    rc = load().exl3_linear_noalloc(_ptr(x), m, _ptr(trellis), _ptr(sign), _ptr(out_scale), n_in, n_out,
+                                    bits_arg(bits, codebook), _ptr(y), _stream(stream))
+    _check(rc, "exl3_linear_noalloc")
+    return y
 
 
 def encode_slot_bytes(bits: int, codebook: int = 0) -> int:

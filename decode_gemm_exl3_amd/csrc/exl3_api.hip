@@ -2,9 +2,16 @@
 #include <atomic>
 #include <climits>
 #include <cstdlib>
+#include <mutex>
 
 #include "../../include/exl3.h"
 #include "exl3_internal.hpp"
+
+// Scratch of exl3_linear_noalloc: one array per GPU, in the library's device
+// code, held from the library's load until the process ends.  In host code its
+// name is a stand-in, not a device address: host code uses only the per-device
+// address that hipGetSymbolAddress returns (noalloc_scratch below).
+static __device__ __align__(256) unsigned char scratch[EXL3_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -30,6 +37,27 @@ int cu_count() {
 }
 
 inline int64_t align256(int64_t v) { return (v + 255) & ~int64_t(255); }
+
+// Device address of `scratch` on the current device, looked up once per device
+// with that device current, or null if the lookup fails.
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+void* noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        (void)hipGetLastError();  // the failed lookup must not surface at an unrelated later call
+        return nullptr;
+    }
+    g_scratch[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
 
 // Most rows exl3_linear hands to the GEMV.
 constexpr int GEMV_LINEAR_MAX_M = 12;
@@ -370,6 +398,22 @@ int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uin
     const bool use_gemv = linear_uses_gemv(m, n_in);
     return use_gemv ? exl3_gemv(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream)
                     : exl3_gemm(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream);
+}
+
+int exl3_linear_noalloc(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+                        const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
+                        void* stream) {
+    // every argument check and the size limit come before any HIP call
+    const int rc = common_checks(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, nullptr, 0, 0);
+    if (rc <= 0) return rc;
+    if (m > EXL3_GEMV_MAX_M || !linear_uses_gemv(m, n_in)) {
+        // the GEMM's rotated input must fit; its split partial sums take what is
+        // left (a smaller split when they do not all fit)
+        if (gemm_rot_bytes(n_in, m) > (int64_t)EXL3_NOALLOC_SCRATCH_BYTES) return EXL3_EUNSUPPORTED;
+    }
+    void* ws = noalloc_scratch();
+    if (!ws) return EXL3_EHIP;
+    return exl3_linear(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, ws, EXL3_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int64_t exl3_encode_slot_bytes(int32_t bits) {

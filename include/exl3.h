@@ -184,6 +184,34 @@ int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uin
                 const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits,
                 uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the static scratch exl3_linear_noalloc uses on each GPU. */
+#define EXL3_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * exl3_linear_noalloc: exl3_linear with no workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  It allocates nothing and calls no
+ * allocating routine: its scratch (the GEMM's rotated input and split partial
+ * sums, the GEMV's rotation pre-pass) is a static device array of
+ * EXL3_NOALLOC_SCRATCH_BYTES in the library, one per GPU, which that GPU holds
+ * from the first call until the process ends.  The array's address on a device
+ * is looked up on the first call on it (with it current).
+ *   Arguments and result as exl3_linear; the caller still owns x, the weights,
+ *   sign, out_scale and y.
+ *   EXL3_EUNSUPPORTED, before any launch, when a GEMM call's rotated input
+ *   (rows * n_in * 2 bytes, rows = m for m <= 128, else m rounded up to a
+ *   multiple of 256) exceeds EXL3_NOALLOC_SCRATCH_BYTES; split partial sums
+ *   that do not fit beside it make the input dimension split less.
+ *   EXL3_EHIP if the scratch's address cannot be looked up.
+ * Given the same split, y equals exl3_linear's bit for bit.  Nothing in the
+ * scratch needs to start at zero, and it keeps the last call's contents.  Calls
+ * on one GPU share its array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race and must be serialised by the caller.
+ */
+int exl3_linear_noalloc(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
+                        const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
+                        void* stream);
+
 /*
  * exl3_encode_slot_bytes: workspace bytes exl3_encode_tiles needs per tile in
  * flight (256 * 2^(16-K): the choice of every trellis step), or EXL3_EINVAL for

@@ -29,7 +29,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) == {"exl3_pack_info", "exl3_decode_tile", "exl3_gemv", "exl3_gemv_multi", "exl3_gemm",
-                          "exl3_linear", "exl3_encode_slot_bytes", "exl3_encode_tiles",
+                          "exl3_linear", "exl3_linear_noalloc", "exl3_encode_slot_bytes", "exl3_encode_tiles",
                           "exl3_status_string"}
     for n in names:
         assert hasattr(lib, n), n
@@ -198,6 +198,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ex, "_LIB", None)
     with pytest.raises(ex.Exl3Error):
         ex.load()
+
+
+def test_noalloc_rejects_before_any_launch(lib):
+    # argument errors, and a GEMM input whose rotation would not fit the static
+    # scratch (8192 rows of 8192 inputs: 128 MiB), return before any HIP call;
+    # m == 0 is a no-op
+    A = 1 << 20  # 16-byte aligned stand-ins: no call below reaches the device
+    f = lib.exl3_linear_noalloc
+    assert f(A, 8192, A, A, A, 8192, 16, 4, A + 64, None) == -2
+    assert f(A, 4097, A, A, A, 8192, 16, 4, A + 64, None) == -2   # 4352 rows: 68 MiB
+    assert f(A, 0, A, A, A, 8192, 16, 4, A + 64, None) == 0
+    assert f(A, -1, A, A, A, 8192, 16, 4, A + 64, None) == -1
+    assert f(A, 4, A, A, A, 100, 16, 4, A + 64, None) == -1
+    assert f(A, 4, A, A, A, 8192, 16, 4, A + 8, None) == -1   # misaligned y
+    assert f(A, 4, 0, A, A, 8192, 16, 4, A + 64, None) == -1  # null trellis
 
 
 def test_gemm_rejects_rotated_input_of_2_gib(lib):
