@@ -115,6 +115,36 @@ def tile_states(words: np.ndarray, K: int) -> np.ndarray:
     return states.reshape(lead + (256,))
 
 
+def tile_row_states(words: np.ndarray, K: int, r) -> np.ndarray:
+    """States 16r .. 16r+15 of packed tiles: one 16-element row of each tile.
+
+    words: uint16 [..., 16K]; r: row index (0..15), broadcastable to
+    words.shape[:-1].  Returns uint16 [..., 16], element c = s_{16r+c}.
+    By FMT-3/4, s_{16r+c} is the 16-bit window at stream bit (16r + c)K; the 16
+    windows of a row lie in the K + 1 words that start at word rK, taken
+    cyclically (row 15 wraps into word 0), so the row is read from that
+    sub-stream: its bit q is stream bit 16rK + q, i.e. bit q % 16 of its word
+    q // 16.  Equal to tile_states(words, K)[..., 16r:16r+16] (pinned in the
+    tests).
+    """
+    _check_k(K)
+    words = np.ascontiguousarray(words, dtype=np.uint16)
+    if words.shape[-1] != 16 * K:
+        raise ValueError("last axis must hold 16*K words")
+    r = np.asarray(r, dtype=np.int64)
+    widx = (r[..., None] * K + np.arange(K + 1)) % (16 * K)        # words of the sub-stream
+    widx = np.broadcast_to(widx, words.shape[:-1] + (K + 1,))
+    sub = np.take_along_axis(words, widx, axis=-1).astype(np.uint32)  # [..., K+1]
+    states = np.empty(sub.shape[:-1] + (16,), dtype=np.uint16)
+    for c in range(16):
+        # sub-stream bits [cK, cK + 16) lie in words w0, w0 + 1 (LSB first),
+        # i.e. bits sh .. sh + 15 of the little-endian pair
+        w0, sh = divmod(c * K, 16)
+        pair = sub[..., w0] | (sub[..., w0 + 1] << np.uint32(16))
+        states[..., c] = (pair >> np.uint32(sh)) & np.uint32(0xFFFF)
+    return states
+
+
 # ---------------------------------------------------------------------------
 # FMT-5: procedural codebook
 # ---------------------------------------------------------------------------
@@ -236,17 +266,27 @@ def linear(x, trellis, sign, out_scale, K, strip_block: int = 64, cb: int = 0) -
     return y * np.asarray(out_scale, np.float64)[None, :]
 
 
-def linear_rows(x, trellis, sign, out_scale, K, rows: np.ndarray, cb: int = 0) -> np.ndarray:
-    """Selected output features only: y[:, rows] (decodes only the strips they lie in)."""
+def weight_rows(trellis, K, rows, cb: int = 0) -> np.ndarray:
+    """Rows W[rows] of the decoded weight matrix as float16 [len(rows), n_in]:
+    row o is row o % 16 of every tile of strip o // 16 (FMT-2), element c of
+    tile column tc at column 16 tc + c."""
+    rows = np.asarray(rows, dtype=np.int64)
+    words = np.asarray(trellis)[rows // 16]                       # [R, tiles_in, 16K]
+    st = tile_row_states(words, K, (rows % 16)[:, None])          # [R, tiles_in, 16]
+    return codebook(st, cb).reshape(rows.size, -1)
+
+
+def linear_rows(x, trellis, sign, out_scale, K, rows: np.ndarray, cb: int = 0,
+                chunk: int = 256) -> np.ndarray:
+    """Selected output features only: y[:, rows] in float64 (decodes only those
+    rows of W, `chunk` rows at a time)."""
     m, n_in, n_out = _check_shapes(x, trellis, sign, out_scale, K)
     rows = np.asarray(rows, dtype=np.int64)
     xr = rotate(np.asarray(x, np.float64), np.asarray(sign, np.float64))
-    strips = np.unique(rows // 16)
     out = np.empty((m, rows.size), dtype=np.float64)
-    for tr in strips:
-        W = dequant(trellis[tr:tr + 1], K, cb).astype(np.float64)  # [16, n_in]
-        sel = np.nonzero(rows // 16 == tr)[0]
-        out[:, sel] = xr @ W[rows[sel] - 16 * tr].T
+    for a in range(0, rows.size, chunk):
+        W = weight_rows(trellis, K, rows[a:a + chunk], cb).astype(np.float64)
+        out[:, a:a + chunk] = xr @ W.T
     return out * np.asarray(out_scale, np.float64)[rows][None, :]
 
 

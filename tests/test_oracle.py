@@ -241,6 +241,30 @@ def test_states_vectorised_equals_scalar(K):
         assert int(st[i]) == O.state_scalar(words, K, i)
 
 
+@pytest.mark.parametrize("K", range(1, 9))
+def test_row_states_equal_tile_states(K):
+    # the row decode reads a (K+1)-word window of the stream: every row of
+    # random tiles, and of a one-hot stream at each bit near the tile's wrap,
+    # against the full-tile states and the scalar bit walk
+    rng = np.random.default_rng(300 + K)
+    words = rng.integers(0, 65536, (5, 16 * K), dtype=np.uint16)
+    full = O.tile_states(words, K)
+    for r in range(16):
+        np.testing.assert_array_equal(O.tile_row_states(words, K, r), full[:, 16 * r:16 * r + 16])
+    rr = rng.integers(0, 16, 5)  # a row per tile
+    got = O.tile_row_states(words, K, rr)
+    for t in range(5):
+        for c in (0, 7, 15):
+            assert int(got[t, c]) == O.state_scalar(words[t], K, 16 * int(rr[t]) + c)
+    nbits = 256 * K
+    for p in list(range(0, 20)) + list(range(nbits - 20, nbits)):
+        w = np.zeros(16 * K, np.uint16)
+        w[p // 16] = 1 << (p % 16)
+        st = O.tile_states(w, K)
+        for r in (0, 1, 14, 15):
+            np.testing.assert_array_equal(O.tile_row_states(w, K, r), st[16 * r:16 * r + 16])
+
+
 def test_states_sliding_recurrence():
     # s_{i+1} = (s_i >> K) | (next K stream bits << (16 - K)), cyclic
     for K in (2, 3, 6):
@@ -333,13 +357,17 @@ def test_linear_scale_and_sign_invariants():
     np.testing.assert_array_equal(y3, y)
 
 
-def test_linear_rows_matches_full():
-    K = 5
-    words, x, sign, scale = synth.random_case(384, 80, K, 2, 13)
-    y = O.linear(x, words, sign, scale, K, strip_block=2)
-    rows = np.array([0, 7, 16, 33, 79, 64])
-    np.testing.assert_allclose(O.linear_rows(x, words, sign, scale, K, rows), y[:, rows],
-                               rtol=1e-12, atol=0)
+@pytest.mark.parametrize("K", range(1, 9))
+def test_linear_rows_matches_full(K):
+    # any rows, in any order, repeated, across chunk boundaries; both codebooks
+    words, x, sign, scale = synth.random_case(384, 80, K, 2, [13, K])
+    rows = np.array([0, 7, 16, 33, 79, 64, 7, 15, 48, 31])
+    for cb in (0, 1):
+        y = O.linear(x, words, sign, scale, K, strip_block=2, cb=cb)
+        np.testing.assert_allclose(O.linear_rows(x, words, sign, scale, K, rows, cb=cb, chunk=3), y[:, rows],
+                                   rtol=1e-12, atol=0)
+        W = O.dequant(words, K, cb)
+        np.testing.assert_array_equal(O.fp16_bits(O.weight_rows(words, K, rows, cb)), O.fp16_bits(W[rows]))
 
 
 def test_oracle_rejects_bad_arguments():
