@@ -204,16 +204,20 @@ def _linear(fn: str, x, trellis, sign, out_scale, bits: int, workspace=None, y=N
     if y is None:
         y = torch.empty((m, n_out), dtype=torch.float16, device=x.device)
     _check_linear(x, trellis, sign, out_scale, bits, y)
-    if workspace is None:
+    if workspace is None and fn != "exl3_gemv":  # the GEMV needs none: it then rotates in every workgroup
         workspace = Workspace(n_in, n_out, bits, max(m, 1), device=x.device)
+    ws_ptr = 0 if workspace is None else _ptr(workspace.buf)
+    ws_bytes = 0 if workspace is None else workspace.nbytes
     rc = getattr(load(), fn)(_ptr(x), m, _ptr(trellis), _ptr(sign), _ptr(out_scale), n_in, n_out,
-                             bits_arg(bits, codebook), _ptr(y), _ptr(workspace.buf), workspace.nbytes, _stream(stream))
+                             bits_arg(bits, codebook), _ptr(y), ws_ptr, ws_bytes, _stream(stream))
     _check(rc, fn)
     return y
 
 
 def gemv(x, trellis, sign, out_scale, bits: int, workspace=None, y=None, stream=None, codebook: int = 0):
-    """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 16 (fp16 out)."""
+    """y = out_scale * (H128(sign * x) @ W^T) for 1 <= m <= 16 (fp16 out).
+
+    Without a workspace nothing beyond y (when not given) is allocated."""
     return _linear("exl3_gemv", x, trellis, sign, out_scale, bits, workspace, y, stream, codebook)
 
 

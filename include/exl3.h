@@ -77,9 +77,14 @@ typedef struct exl3_pack_info_t {
 } exl3_pack_info_t;
 
 /*
- * exl3_pack_info: sizes of the packed weight and of the workspace.
+ * exl3_pack_info: sizes of the packed weight and of the workspace (pages:
+ * "Viterbi encoding kernel" - the weight is quantised in 16x16 blocks, each
+ * block's code packed as a sequence of 16-bit indices; here 16*K words per
+ * block, K bits per weight).
  *   n_in % 128 == 0, n_out % 16 == 0, 1 <= K <= 8, max_m >= 1.
- * Host-only; never touches the GPU.  Returns EXL3_EINVAL on bad arguments.
+ *   out : filled on success; max_m is echoed, reserved is set to 0.
+ * Host-only; never touches the GPU.  Returns EXL3_EINVAL on bad arguments
+ * (out untouched).
  */
 int exl3_pack_info(int32_t n_in, int32_t n_out, int32_t bits, int32_t max_m,
                    exl3_pack_info_t* out);

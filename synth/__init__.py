@@ -118,6 +118,60 @@ def llama8b_stack(n_layers: int = 32) -> list[Matmul]:
     return out
 
 
+# --- the launches the benchmark times ----------------------------------------
+# A launch is one call: a GEMV launch may serve several projections that read
+# the same input (gate and up, q/k/v), drawn member by member with their own
+# seeds by `draw_group` (the first member's x and sign serve the launch).
+@dataclass
+class Launch:
+    name: str
+    members: list
+
+    @property
+    def K(self) -> int:
+        return self.members[0].K
+
+    @property
+    def n_in(self) -> int:
+        return self.members[0].n_in
+
+    @property
+    def m(self) -> int:
+        return self.members[0].m
+
+    @property
+    def n_outs(self) -> list:
+        return [mm.n_out for mm in self.members]
+
+
+def mlp_launches(K: int, m: int = 1) -> list[Launch]:
+    """The Llama-3.1-8B MLP at K bits and m rows as it is launched: gate and up
+    (4096->14336 each) in one fused launch, then down (14336->4096)."""
+    gate = Matmul(f"gate_k{K}_m{m}", 4096, 14336, K, m, [0, 2, K, m, 0])
+    up = Matmul(f"up_k{K}_m{m}", 4096, 14336, K, m, [0, 2, K, m, 1])
+    down = Matmul(f"down_k{K}_m{m}", 14336, 4096, K, m, [0, 2, K, m, 2])
+    return [Launch(f"gate_up_k{K}", [gate, up]), Launch(f"down_k{K}", [down])]
+
+
+def llama70b_launches() -> list[Launch]:
+    """70B-shaped decode launches at m=1: gate and up (8192->28672 each) fused
+    at K=2 and K=3, down (28672->8192) at K=2 and K=3, and the 8192->8192
+    attention projection at K=4."""
+    out = []
+    for K in (2, 3):
+        out.append(Launch(f"gate_up_k{K}", [Matmul(f"gate70_k{K}", 8192, 28672, K, 1, [0, 3, K, 0]),
+                                            Matmul(f"up70_k{K}", 8192, 28672, K, 1, [0, 3, K, 1])]))
+    for K in (2, 3):
+        out.append(Launch(f"down_k{K}", [Matmul(f"down70_k{K}", 28672, 8192, K, 1, [0, 3, K, 2])]))
+    out.append(Launch("attn_k4", [Matmul("attn70_k4", 8192, 8192, 4, 1, [0, 3, 4, 3])]))
+    return out
+
+
+def medium_m(m: int, n_in: int = 4096, n_out: int = 14336, K: int = 4) -> Matmul:
+    """Batched decode and chunked prefill sizes of the 8B gate projection."""
+    return Matmul(f"medium_m{m}", n_in, n_out, K, m, [0, 8, n_in, n_out, K, m])
+
+
 # --- projections fed by one input (one fused GEMV launch) ---------------------
 STACK_GROUPS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
 

@@ -65,3 +65,30 @@ def test_decode_and_encode_reject_bad_tensors():
         ex.encode_tiles(w, 3, workspace=ws, costs=torch.empty(3, dtype=torch.float32))
     with pytest.raises(ex.Exl3Error, match="must be on a GPU device"):
         ex.encode_tiles(w, 3, workspace=ws)
+
+
+def test_gemv_without_workspace_allocates_none(monkeypatch):
+    # gemv() hands the library a null workspace instead of allocating one per
+    # call (the GEMV needs none); gemm() and linear() still size one
+    calls = []
+
+    class FakeLib:
+        def __getattr__(self, name):
+            def f(*args):
+                calls.append((name, args))
+                return 0
+            return f
+
+    def no_workspace(*a, **k):
+        raise AssertionError("a workspace was allocated")
+
+    monkeypatch.setattr(ex, "load", lambda: FakeLib())
+    monkeypatch.setattr(ex, "_on_gpu", lambda **t: None)
+    monkeypatch.setattr(ex, "_stream", lambda s: 0)
+    monkeypatch.setattr(ex, "Workspace", no_workspace)
+    x, tr, sign, sc, y = case()
+    ex.gemv(x, tr, sign, sc, 3, y=y)
+    name, args = calls[-1]
+    assert name == "exl3_gemv" and args[9] == 0 and args[10] == 0
+    with pytest.raises(AssertionError, match="workspace was allocated"):
+        ex.gemm(x, tr, sign, sc, 3, y=y)
