@@ -100,3 +100,45 @@ def test_encode_codebook1():
     words, cost = O.encode_tile(w, 3, cb=1)
     dec = O.decode_tiles(words, 3, cb=1).astype(np.float64)
     assert abs(((w - dec) ** 2).sum() - float(cost)) <= 1e-5 * float(cost)
+
+
+# ------------------------------ the two-pass reading against the exact optimum
+GAP_FILE = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden", "encoder_tail_biting_gap.txt")
+
+
+def _gap_rows():
+    rows = []
+    with open(GAP_FILE) as f:
+        for ln in f:
+            if ln.strip() and not ln.startswith("#"):
+                K, t, c2, ce = ln.split()
+                rows.append((int(K), int(t), np.float32(c2), np.float32(ce)))
+    return rows
+
+
+def _gap_target(K, t):
+    # the targets make_encoder_gap.py drew (its recipe, restated)
+    return np.random.default_rng([0, 9, K, t]).standard_normal(256).astype(np.float32)
+
+
+def test_two_pass_costs_recorded_and_never_below_the_exact_optimum():
+    # 28 unit-Gaussian tiles at K = 5..8 (16-bit state): the encoder's two-pass
+    # search, rerun here, gives the recorded cost, which is never below the
+    # recorded exact tail-biting optimum (the best of all 2^(16-K) constrained
+    # searches); on these tiles the two are equal
+    vals = O.codebook(np.arange(65536)).astype(np.float32)
+    rows = _gap_rows()
+    assert len(rows) == 28 and {r[0] for r in rows} == {5, 6, 7, 8}
+    for K, t, c2, ce in rows:
+        path, c = O.tail_biting_two_pass(_gap_target(K, t), vals, 16, K)
+        assert c == c2, (K, t, c, c2)
+        assert c2 >= ce, (K, t)
+        assert path[-1] >> K == path[0] & ((1 << (16 - K)) - 1)
+
+
+def test_recorded_exact_optimum_k8():
+    # one recorded exact optimum recomputed (256 constrained searches)
+    vals = O.codebook(np.arange(65536)).astype(np.float32)
+    K, t, _, ce = _gap_rows()[-8]
+    assert K == 8
+    assert O.tail_biting_exact(_gap_target(K, t), vals, 16, K)[1] == ce
