@@ -1,30 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of the EXL3 decode-matmul on one MI355X.
 
-Workload (the headline GEMV case): the Llama-3.1-8B-shaped MLP at m=1 -
-gate and up 4096->14336 and down 14336->4096 - at K = 2, 3 and 4 bits per
-weight.  One step = those 9 projections, inputs resident in HBM: per K, gate
-and up in one exl3_gemv_multi launch (they read the same input) and down
-through exl3_gemv.
-The weight buffers are replicated so that consecutive steps read different
-memory (more than 1 GiB in rotation), so the 256 MB Infinity Cache cannot
-serve the stream.  Steps run as HIP graphs replayed on one stream.
+Headline workload: the 32-layer Llama-3.1-8B-shaped linear stack at m=1 (per
+layer q 4096->4096, k/v 4096->1024, o 4096->4096, gate/up 4096->14336, down
+14336->4096; per-layer K drawn from {2..6}, attention +1 bit; 224 matmuls, about
+4 GB of packed weights).  One step = one token: every matmul of every layer, in
+model order, on one stream, q/k/v and gate/up each in one exl3_gemv_multi launch
+(128 launches), replayed as one HIP graph.  Inputs are resident in HBM; the
+stack's weights exceed every cache, so each step streams them from HBM.
 
 value = algorithmic bytes of a step / time of a step (GB/s):
-  per launch: K/8 bytes per weight + x (2 m n_in) + sign (2 n_in) once, and
-  per projection out_scale (2 n_out) + y (2 m n_out).
-roofline: the dominant kernel (the fused gate+up launch at K=4), algorithmic
-bytes per launch over its average launch time from HIP events around a batch
-of back-to-back launches; alu_roofline: the same launch's vector instructions
-(committed counters) against the vector-ALU issue peak.
-cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+  per launch: K/8 bytes per weight + x (2 m n_in) + sign (2 n_in) once, and per
+  projection out_scale (2 n_out) + y (2 m n_out).
+roofline: the launch shape with the largest share of the step's time (count in
+  the step x its average duration), its algorithmic bytes per launch over its
+  average duration from HIP events around back-to-back launches on the stream
+  they run on, with at least 1 GiB of distinct weights in rotation; beside it
+  the median of the committed rocprofv3 kernel trace of the same launch shape
+  and the HBM traffic from the committed counters (both only while the kernel
+  sources are those they were taken on).
+cpu_baseline: the CPU oracle on a bounded sample of every workload (decode and
+  contraction timed apart, all host cores), run before the GPU is touched.
+extra: every other workload (the single 4096x4096 layer, the 8B MLP at m = 1,
+  4, 8, the 70B launches, the m=2048 GEMMs, medium m, codebook 1, the encoder,
+  the unfused stack, a device copy), each per-launch figure over at least 1 GiB
+  of distinct weights in rotation.
 
-Prints one JSON line.
+Prints one JSON line.  --only runs one launch shape for the profiler;
+--trace-summary summarises a rocprofv3 kernel trace.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -36,87 +45,112 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0
+GIB = 1 << 30
+# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+# (one 32-bit lane-operation per lane and clock; a wave64 instruction takes
+# four clocks of a SIMD).
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
 
 
-def gemv_bytes(n_in, n_out, K, m):
-    return n_in * n_out * K // 8 + 2 * m * n_in + 2 * n_in + 2 * n_out + 2 * m * n_out
-
-
-def call_bytes(c):
+# ----------------------------------------------------------------- launches --
+def launch_bytes(launch) -> int:
     """Algorithmic bytes of one launch: each projection's weights, scale and y,
     plus x and sign once (they are read once for the whole launch)."""
-    b = 2 * c["m"] * c["n_in"] + 2 * c["n_in"]
-    for n_out in c["n_outs"]:
-        b += c["n_in"] * n_out * c["K"] // 8 + 2 * n_out + 2 * c["m"] * n_out
+    m, n_in, K = launch.m, launch.n_in, launch.K
+    b = 2 * m * n_in + 2 * n_in
+    for n_out in launch.n_outs:
+        b += n_in * n_out * K // 8 + 2 * n_out + 2 * m * n_out
     return b
 
 
-def make_call(torch, name, K, n_in, n_outs, m, words_list, x, sign, scales, replicas):
-    """Device tensors of one launch (one or more projections of one input)."""
-    reps = []
-    for w in words_list:
-        wd = torch.from_numpy(w.view(np.int16)).cuda()
-        reps.append([wd] + [wd.clone() for _ in range(replicas - 1)])
-    c = dict(name=name, K=K, n_in=n_in, n_outs=list(n_outs), m=m, words=reps,
-             x=torch.from_numpy(x).cuda(), sign=torch.from_numpy(sign).cuda(),
-             scales=[torch.from_numpy(sc).cuda() for sc in scales],
-             ys=[torch.empty((m, n_out), dtype=torch.float16, device="cuda") for n_out in n_outs])
-    c["bytes"] = call_bytes(c)
-    return c
+def weight_bytes(launch) -> int:
+    return sum(mm.trellis_bytes for mm in launch.members)
 
 
-def build_mlp(torch, ex, m, Ks=(2, 3, 4), replicas=7, seed_base=0):
-    """The MLP launches per K: gate and up in one fused launch (they read the
-    same input), then down; `replicas` copies of every weight matrix."""
-    import synth
-    calls = []
-    for K in Ks:
-        seeds = {nm: [seed_base, 2, K, i] for i, nm in enumerate(("gate", "up", "down"))}
-        words = {nm: synth.words_only(n_in, n_out, K, seeds[nm])
-                 for nm, n_in, n_out in (("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096))}
-        for name, n_in, members in (("gate_up", 4096, ("gate", "up")), ("down", 14336, ("down",))):
-            rng = np.random.default_rng(seeds[members[0]] + [1])
-            x = rng.standard_normal((m, n_in)).astype(np.float16)
-            sign = (2 * rng.integers(0, 2, n_in) - 1).astype(np.float16)
-            n_outs = [words[nm].shape[0] * 16 for nm in members]
-            scales = [(rng.uniform(0.5, 1.5, n) * 0.02).astype(np.float16) for n in n_outs]
-            calls.append(make_call(torch, f"{name}_k{K}", K, n_in, n_outs, m, [words[nm] for nm in members],
-                                   x, sign, scales, replicas))
-    return calls
+def replicas_for(launch, min_bytes=GIB) -> int:
+    """Copies of the weights so that at least min_bytes of distinct weights
+    rotate (the 256 MB Infinity Cache then cannot serve a repeated launch)."""
+    return max(1, math.ceil(min_bytes / weight_bytes(launch)))
 
 
-def launch(ex, c, rep):
-    cb = c.get("codebook", 0)
-    if len(c["n_outs"]) == 1:
-        ex.gemv(c["x"], c["words"][0][rep], c["sign"], c["scales"][0], c["K"], y=c["ys"][0], codebook=cb)
-    else:
-        ex.gemv_multi(c["x"], [(w[rep], sc) for w, sc in zip(c["words"], c["scales"])], c["sign"], c["K"],
-                      ys=c["ys"], codebook=cb)
+def stack_kind(launch) -> str:
+    names = [mm.name.split(".")[1].split("_k")[0] for mm in launch.members]
+    return {"q+k+v": "qkv"}.get("+".join(names), "+".join(names).replace("gate+up", "gate_up"))
 
 
-def run_step(ex, calls, rep):
-    for c in calls:
-        launch(ex, c, rep % len(c["words"][0]))
+class DevLaunch:
+    """Device tensors of one launch: `replicas` copies of every weight matrix,
+    one input, scales and outputs; `fn` is the binding call that runs it."""
+
+    def __init__(self, torch, ex, launch, fn, replicas=1, workspace=None, codebook=0, name=None):
+        import synth
+        words, x, sign, scales = synth.draw_group(launch.members)
+        self.launch, self.fn, self.cb, self.ws = launch, fn, codebook, workspace
+        self.name = name or launch.name
+        self.words = []
+        for w in words:
+            wd = torch.from_numpy(w.view(np.int16)).cuda()
+            self.words.append([wd] + [wd.clone() for _ in range(replicas - 1)])
+        self.replicas = replicas
+        self.x = torch.from_numpy(x).cuda()
+        self.sign = torch.from_numpy(sign).cuda()
+        self.scales = [torch.from_numpy(sc).cuda() for sc in scales]
+        self.ys = [torch.empty((launch.m, n), dtype=torch.float16, device="cuda") for n in launch.n_outs]
+        self.bytes = launch_bytes(launch)
+
+    def call(self, ex, rep=0):
+        r = rep % self.replicas
+        if self.fn == "gemv_multi":
+            ex.gemv_multi(self.x, [(w[r], sc) for w, sc in zip(self.words, self.scales)], self.sign, self.launch.K,
+                          ys=self.ys, workspace=self.ws, codebook=self.cb)
+        else:
+            getattr(ex, self.fn)(self.x, self.words[0][r], self.sign, self.scales[0], self.launch.K,
+                                 workspace=self.ws, y=self.ys[0], codebook=self.cb)
 
 
-def time_graphs(torch, ex, calls, replicas, steps, warmup, per_graph=1):
-    """ms per step from HIP graphs replayed on one stream.  Graph r holds
-    `per_graph` steps on weight replicas r, r+1, ...; short steps need several
-    per graph so that the host's replay rate does not set the time."""
-    stream = torch.cuda.Stream()
-    graphs = []
-    with torch.cuda.stream(stream):
-        run_step(ex, calls, 0)  # first call caches device properties outside capture
+def gemv_fn(launch) -> str:
+    return "gemv_multi" if len(launch.members) > 1 else "gemv"
+
+
+def time_events(torch, ex, dl, n):
+    """Average ms per launch: HIP events on the stream the library launches on
+    (the current stream) around n back-to-back launches, weight replicas
+    rotating.  A GPU sleep first, so that every launch is queued before the GPU
+    reaches it and the events time the GPU, not the host's launch rate."""
+    dl.call(ex, 0)
     torch.cuda.synchronize()
-    for r in range(replicas):
+    stream = torch.cuda.current_stream()
+    torch.cuda._sleep(int(5e7))
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        dl.call(ex, i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def time_graphs(torch, ex, step_fn, variants, steps, warmup, per_graph=1):
+    """ms per step from HIP graphs replayed on one stream.  Graph v holds
+    `per_graph` steps on weight replicas v, v+1, ...; short steps need several
+    per graph so that the host's replay rate does not set the time.  The timed
+    region is bracketed by synchronisations and HIP events on the replay
+    stream."""
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        step_fn(0)  # first call caches device properties outside capture
+    torch.cuda.synchronize()
+    graphs = []
+    for v in range(variants):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
             for k in range(per_graph):
-                run_step(ex, calls, r + k)
+                step_fn(v + k)
         graphs.append(g)
     torch.cuda.synchronize()
     for i in range(warmup):
-        graphs[i % replicas].replay()
+        graphs[i % variants].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
@@ -124,79 +158,180 @@ def time_graphs(torch, ex, calls, replicas, steps, warmup, per_graph=1):
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(steps):
-            graphs[i % replicas].replay()
+            graphs[i % variants].replay()
         e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / (steps * per_graph), wall
 
 
-def per_kernel_events(torch, ex, calls, replicas, steps):
-    """Average duration of each launch shape: HIP events on the stream the
-    library launches on (the current stream) around `steps` back-to-back
-    launches of that shape (weight replicas rotating), divided by `steps`."""
-    stream = torch.cuda.current_stream()
-    ev = []
-    for c in calls:
-        # a long GPU sleep before each batch, so that all its launches are
-        # queued before the GPU reaches them and the events time the GPU, not
-        # the host's launch rate
-        torch.cuda._sleep(int(5e7))
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(steps):
-            launch(ex, c, i % replicas)
-        b.record(stream)
-        ev.append((c["name"], a, b))
-    torch.cuda.synchronize()
-    return {name: a.elapsed_time(b) / steps for name, a, b in ev}
+def gbs(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
 
 
-def copy_bandwidth(torch, nbytes=1 << 30, iters=10):
-    a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    return 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
-
-
-def gemm_tflops(torch, ex, iters=5, codebook=0, n_out=8192, K=4):
-    """Prefill GEMM: m=2048, 8192->8192 at K=4, or 8192->n_out at K (the second metric)."""
+# -------------------------------------------------------- the 8B stack ------
+def stack_launches(fused=True):
     import synth
-    m, n_in = 2048, 8192
-    w = torch.from_numpy(synth.words_only(n_in, n_out, K, [0, 4, 9] if (n_out, K) == (8192, 4) else [0, K, 9, n_out])
-                         .view(np.int16)).cuda()
-    x = torch.randn((m, n_in), device="cuda").half()
-    sign = torch.ones(n_in, dtype=torch.float16, device="cuda")
-    scale = torch.full((n_out,), 0.02, dtype=torch.float16, device="cuda")
-    y = torch.empty((m, n_out), dtype=torch.float16, device="cuda")
-    ws = ex.Workspace(n_in, n_out, K, m)
-    ex.gemm(x, w, sign, scale, K, workspace=ws, y=y, codebook=codebook)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(iters):
-        ex.gemm(x, w, sign, scale, K, workspace=ws, y=y, codebook=codebook)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / iters
-    return 2.0 * m * n_in * n_out / (ms * 1e-3) / 1e12, ms
+    if fused:
+        return [synth.Launch("+".join(mm.name for mm in g), g) for g in synth.llama8b_stack_groups()]
+    return [synth.Launch(mm.name, [mm]) for mm in synth.llama8b_stack()]
+
+
+def stack_shapes(launches):
+    """Distinct launch shapes of the stack: key -> (count, first launch)."""
+    shapes = {}
+    for lc in launches:
+        key = f"{stack_kind(lc)}_k{lc.K}"
+        cnt, first = shapes.get(key, (0, lc))
+        shapes[key] = (cnt + 1, first)
+    return shapes
+
+
+def stack_run(torch, ex, steps, warmup, fused=True):
+    """Tokens/s of the stack: one HIP graph of every launch of a token."""
+    launches = stack_launches(fused)
+    dls = [DevLaunch(torch, ex, lc, gemv_fn(lc)) for lc in launches]
+    nbytes = sum(d.bytes for d in dls)
+
+    def step(_v):
+        for d in dls:
+            d.call(ex, 0)
+
+    ms, wall = time_graphs(torch, ex, step, 1, steps, warmup)
+    del dls
+    torch.cuda.empty_cache()
+    return {"tokens_per_s": round(1e3 / ms, 1), "ms_per_token": round(ms, 5), "launches": len(launches),
+            "gbs": round(gbs(nbytes, ms), 1), "bytes_per_token": nbytes, "wall_s": round(wall, 3)}
+
+
+def stack_shape_times(torch, ex, n=50):
+    """Average duration of every distinct launch shape of the fused stack, over
+    >= 1 GiB of weights in rotation, and its share of a token's time."""
+    out = {}
+    for key, (cnt, lc) in stack_shapes(stack_launches(True)).items():
+        dl = DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=replicas_for(lc))
+        ms = time_events(torch, ex, dl, max(n, dl.replicas))
+        out[key] = {"count": cnt, "us": round(ms * 1e3, 3), "bytes_per_launch": dl.bytes,
+                    "gbs": round(gbs(dl.bytes, ms), 1), "rotation_bytes": dl.replicas * weight_bytes(lc),
+                    "n_in": lc.n_in, "n_outs": lc.n_outs, "K": lc.K, "total_us": round(cnt * ms * 1e3, 2)}
+        del dl
+        torch.cuda.empty_cache()
+    total = sum(v["total_us"] for v in out.values())
+    for v in out.values():
+        v["share"] = round(v["total_us"] / total, 4)
+    return out
+
+
+# -------------------------------------------------------------- profiles ----
+def kernel_sources_hash() -> str:
+    """Hash of the GEMV kernel and launch-plan sources with comments and blank
+    lines removed: profile-derived figures are valid only for this code."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for f in ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip"):
+        with open(os.path.join(ROOT, "decode_gemm_exl3_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
+    return h.hexdigest()[:16]
+
+
+def profile_record(name):
+    """A committed profile summary (JSON) of the current sources, or None."""
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("kernel_sources_hash") == kernel_sources_hash() else None
+
+
+# ----------------------------------------------------------- other configs --
+def single_layer_rate(torch, ex, n=128):
+    """The single 4096x4096 layer at K=4, m=1 through exl3_gemv, 128 copies of
+    its 8 MiB of weights in rotation."""
+    import synth
+    mm = synth.single_layer()[0]
+    lc = synth.Launch(mm.name, [mm])
+    dl = DevLaunch(torch, ex, lc, "gemv", replicas=replicas_for(lc))
+    ms = time_events(torch, ex, dl, max(n, dl.replicas))
+    out = {"us": round(ms * 1e3, 3), "gbs": round(gbs(dl.bytes, ms), 1), "bytes": dl.bytes,
+           "rotation_bytes": dl.replicas * weight_bytes(lc)}
+    del dl
+    torch.cuda.empty_cache()
+    return out
+
+
+def mlp_rates(torch, ex, m, steps, n=50):
+    """The 8B MLP at m rows, K = 2, 3, 4 (gate+up fused, down): per-launch
+    figures over >= 1 GiB of rotation, and the step of all six launches as
+    graphs over enough replicas to rotate >= 1 GiB."""
+    import synth
+    ws = ex.Workspace(14336, 14336, 8, m)
+    launches = [lc for K in (2, 3, 4) for lc in synth.mlp_launches(K, m)]
+    per = {}
+    for lc in launches:
+        dl = DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=replicas_for(lc), workspace=ws)
+        ms = time_events(torch, ex, dl, max(n, dl.replicas))
+        per[lc.name] = {"us": round(ms * 1e3, 3), "gbs": round(gbs(dl.bytes, ms), 1),
+                        "rotation_bytes": dl.replicas * weight_bytes(lc)}
+        del dl
+        torch.cuda.empty_cache()
+    step_w = sum(weight_bytes(lc) for lc in launches)
+    reps = max(1, math.ceil(GIB / step_w))
+    dls = [DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=reps, workspace=ws) for lc in launches]
+    nbytes = sum(d.bytes for d in dls)
+
+    def step(v):
+        for d in dls:
+            d.call(ex, v)
+
+    ms, _ = time_graphs(torch, ex, step, reps, steps, 5)
+    del dls
+    torch.cuda.empty_cache()
+    return {"step_gbs": round(gbs(nbytes, ms), 1), "step_us": round(ms * 1e3, 2),
+            "step_rotation_bytes": reps * step_w, "launches": per}
+
+
+def llama70b_rates(torch, ex, n=40):
+    import synth
+    ws = ex.Workspace(28672, 28672, 8, 1)
+    out = {}
+    for lc in synth.llama70b_launches():
+        dl = DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=replicas_for(lc), workspace=ws)
+        ms = time_events(torch, ex, dl, max(n, dl.replicas))
+        out[lc.name] = {"us": round(ms * 1e3, 2), "gbs": round(gbs(dl.bytes, ms), 1),
+                        "rotation_bytes": dl.replicas * weight_bytes(lc)}
+        del dl
+        torch.cuda.empty_cache()
+    return out
+
+
+def gemm_rate(torch, ex, which, codebook=0, n=None):
+    """Prefill GEMM at m=2048 (8192->8192 K=4 or 8192->28672 K=3), the whole
+    call (rotation pre-pass and GEMM) timed by events, weights rotating over
+    >= 1 GiB."""
+    import synth
+    mm = synth.prefill_gemm()[0 if which == "8192_k4" else 1]
+    lc = synth.Launch(mm.name, [mm])
+    ws = ex.Workspace(mm.n_in, mm.n_out, mm.K, mm.m)
+    dl = DevLaunch(torch, ex, lc, "gemm", replicas=replicas_for(lc), workspace=ws, codebook=codebook)
+    ms = time_events(torch, ex, dl, n or max(20, dl.replicas))
+    tf = 2.0 * mm.m * mm.n_in * mm.n_out / (ms * 1e-3) / 1e12
+    out = {"tflops": round(tf, 1), "us": round(ms * 1e3, 1), "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+           "rotation_bytes": dl.replicas * weight_bytes(lc)}
+    del dl, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def fp16_matmul_tflops(torch, iters=10):
     """Context for the GEMM: a plain fp16 matrix product of the same shape
     (2048 x 8192 by 8192 x 8192, no decode) through torch's BLAS on the same
-    GPU: what the vendor library reaches on this part, at the clock the matrix
-    cores hold on random data."""
+    GPU: what the vendor library reaches on this part."""
     m, k, n = 2048, 8192, 8192
     a = torch.randn((m, k), device="cuda").half()
     b = torch.randn((k, n), device="cuda").half()
@@ -211,182 +346,39 @@ def fp16_matmul_tflops(torch, iters=10):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters
     del a, b, c
-    return 2.0 * m * k * n / (ms * 1e-3) / 1e12, ms
+    return {"tflops": round(2.0 * m * k * n / (ms * 1e-3) / 1e12, 1), "us": round(ms * 1e3, 1)}
 
 
-def cpu_baseline():
-    """The CPU oracle on a bounded sample of the workload: the K=4 MLP at m=1
-    (gate and up 4096->14336, down 14336->4096), one BLAS thread."""
+def medium_m_rates(torch, ex, ms=(16, 32, 64, 128, 256), n=40):
+    """Batched decode and chunked prefill sizes of the 8B gate projection
+    (4096->14336, K=4) through exl3_linear (the GEMV or the split GEMM, as its
+    table picks)."""
     import synth
-    from oracle import exl3_oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    K, m = 4, 1
-    mats = [(nm, n_in, n_out, [0, 2, K, i]) for i, (nm, n_in, n_out) in
-            enumerate((("gate", 4096, 14336), ("up", 4096, 14336), ("down", 14336, 4096)))]
-    inputs = []
-    for nm, n_in, n_out, seed in mats:
-        w = synth.words_only(n_in, n_out, K, seed)
-        rng = np.random.default_rng(seed + [1])
-        x = rng.standard_normal((m, n_in)).astype(np.float16)
-        sign = (2 * rng.integers(0, 2, n_in) - 1).astype(np.float16)
-        scale = (rng.uniform(0.5, 1.5, n_out) * 0.02).astype(np.float16)
-        inputs.append((w, x, sign, scale, gemv_bytes(n_in, n_out, K, m)))
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    t0 = time.perf_counter()
-    for w, x, sign, scale, _ in inputs:
-        O.linear(x, w, sign, scale, K)
-    dt = time.perf_counter() - t0
-    if ctx is not None and hasattr(ctx, "unregister"):
-        ctx.unregister()
-    nbytes = sum(i[-1] for i in inputs)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the K=4 MLP at m=1 (gate, up 4096->14336, down 14336->4096; 3 of the 9 projections "
-                      f"of a step), {dt:.1f} s, numpy fp64, BLAS limited to 1 thread"}
-
-
-def kernel_sources_hash() -> str:
-    """Hash of the GEMV kernel and launch-plan sources with their comments and
-    blank lines removed: counter-derived figures are valid only for this code."""
-    import hashlib
-    import re
-    h = hashlib.sha256()
-    for f in ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip"):
-        with open(os.path.join(ROOT, "decode_gemm_exl3_amd", "csrc", f), encoding="utf-8") as fh:
-            text = fh.read()
-        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
-        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
-    return h.hexdigest()[:16]
-
-
-def recorded_traffic():
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    profile (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the
-    kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "gemv_gate_up_k4_llama8b_traffic.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_sources_hash") != kernel_sources_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
-
-
-# Vector-ALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-# (one 32-bit lane-operation per lane and clock; a wave64 instruction takes
-# four clocks of a SIMD).
-VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
-
-
-def alu_roofline(ms_per_launch):
-    """The same launch against the vector-ALU issue peak: the decode makes the
-    GEMV issue-bound at K <= 4, so this is the roofline that binds."""
-    n = recorded_valu_insts()
-    if n is None:
-        return None
-    achieved = n * 64 / (ms_per_launch * 1e-3)
-    return {"bound": "alu", "kernel": "gemv_kernel<K=4> gate+up 4096->2x14336",
-            "achieved": round(achieved / 1e12, 2), "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
-            "unit": "T lane-ops/s", "frac": round(achieved / VALU_PEAK_LANE_OPS, 4),
-            "valu_insts_per_launch": int(n)}
-
-
-def recorded_valu_insts():
-    """Vector-ALU instructions (MFMAs excluded) per launch of the dominant
-    kernel from the committed counter profile, or None when the kernel
-    sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", "gemv_gate_up_k4_llama8b_issue.json")
-    try:
-        with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if rec.get("kernel_sources_hash") != kernel_sources_hash():
-        return None
-    return rec.get("valu_insts_without_mfma")
-
-
-def stack_tokens_per_s(torch, ex, fused=True, reps=20):
-    """32-layer Llama-3.1-8B-shaped stack at m=1: tokens/s = 1 / (one graph
-    replay of every projection of every layer, in model order, on one stream).
-    fused: q/k/v and gate/up each in one launch (128 launches), else one launch
-    per matmul (224).  The stack's weights (about 4 GB) exceed every cache."""
-    import synth
-    groups = synth.llama8b_stack_groups()
-    calls = []
-    for grp in groups:
-        parts = [grp] if fused else [[mm] for mm in grp]
-        for part in parts:
-            words, x, sign, scales = synth.draw_group(part)
-            calls.append(make_call(torch, "+".join(mm.name for mm in part), part[0].K, part[0].n_in,
-                                   [mm.n_out for mm in part], 1, words, x, sign, scales, 1))
-    nbytes = sum(c["bytes"] for c in calls)
-    ms, _ = time_graphs(torch, ex, calls, 1, reps, 3)
-    out = {"tokens_per_s": round(1e3 / ms, 1), "ms_per_token": round(ms, 4), "launches": len(calls),
-           "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_token": nbytes}
-    del calls
-    torch.cuda.empty_cache()
-    return out
-
-
-def llama70b_rates(torch, ex, replicas=3, steps=20):
-    """70B-shaped decode GEMVs at m=1: GB/s of each launch shape."""
-    import synth
+    ws = ex.Workspace(4096, 14336, 4, max(ms))
     out = {}
-    for name, n_in, n_outs, K in (("gate_up_k2", 8192, (28672, 28672), 2), ("gate_up_k3", 8192, (28672, 28672), 3),
-                                  ("down_k2", 28672, (8192,), 2), ("down_k3", 28672, (8192,), 3),
-                                  ("attn_k4", 8192, (8192,), 4)):
-        words = [synth.words_only(n_in, n, K, [0, 3, 100 + i, K]) for i, n in enumerate(n_outs)]
-        rng = np.random.default_rng([0, 3, 200, K, n_in])
-        x = rng.standard_normal((1, n_in)).astype(np.float16)
-        sign = (2 * rng.integers(0, 2, n_in) - 1).astype(np.float16)
-        scales = [(rng.uniform(0.5, 1.5, n) * 0.02).astype(np.float16) for n in n_outs]
-        c = make_call(torch, name, K, n_in, n_outs, 1, words, x, sign, scales, replicas)
-        ms, _ = time_graphs(torch, ex, [c], replicas, steps, 3, per_graph=12)
-        out[name] = {"gbs": round(c["bytes"] / (ms * 1e-3) / 1e9, 1), "us": round(ms * 1e3, 2)}
-        del c
+    for m in ms:
+        mm = synth.medium_m(m)
+        lc = synth.Launch(mm.name, [mm])
+        dl = DevLaunch(torch, ex, lc, "linear", replicas=replicas_for(lc), workspace=ws)
+        t = time_events(torch, ex, dl, max(n, dl.replicas))
+        out[f"m{m}"] = {"us": round(t * 1e3, 1), "weight_gbs": round(gbs(weight_bytes(lc), t), 1),
+                        "tflops": round(2.0 * m * mm.n_in * mm.n_out / (t * 1e-3) / 1e12, 1)}
+        del dl
         torch.cuda.empty_cache()
     return out
 
 
-def medium_m(torch, ex, ms=(16, 32, 64, 128, 256), n_in=4096, n_out=14336, K=4, replicas=4):
-    """Batched decode and chunked prefill sizes through exl3_linear (the GEMV or
-    the split GEMM, as its table picks): us per call, weight GB/s and TFLOP/s."""
+def codebook1_rates(torch, ex, n=50):
+    """The byte-sum codebook on the K=4 MLP launches at m=1 and the 8192x8192 GEMM."""
     import synth
-    w = torch.from_numpy(synth.words_only(n_in, n_out, K, [0, 8, K]).view(np.int16)).cuda()
-    reps = [w] + [w.clone() for _ in range(replicas - 1)]
-    sign = torch.ones(n_in, dtype=torch.float16, device="cuda")
-    scale = torch.full((n_out,), 0.02, dtype=torch.float16, device="cuda")
-    ws = ex.Workspace(n_in, n_out, K, max(ms))
     out = {}
-    for m in ms:
-        x = torch.randn((m, n_in), device="cuda").half()
-        y = torch.empty((m, n_out), dtype=torch.float16, device="cuda")
-        for i in range(2):
-            ex.linear(x, reps[i % replicas], sign, scale, K, workspace=ws, y=y)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        st = torch.cuda.Stream()
-        with torch.cuda.graph(g, stream=st):
-            for i in range(8):
-                ex.linear(x, reps[i % replicas], sign, scale, K, workspace=ws, y=y)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(5):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / 40 * 1e3
-        out[f"m{m}"] = {"us": round(us, 1), "weight_gbs": round(n_in * n_out * K / 8 / us / 1e3, 1),
-                        "tflops": round(2.0 * m * n_in * n_out / us / 1e6, 1)}
+    for lc in synth.mlp_launches(4, 1):
+        dl = DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=replicas_for(lc), codebook=1)
+        ms = time_events(torch, ex, dl, max(n, dl.replicas))
+        out[lc.name] = {"us": round(ms * 1e3, 2), "gbs": round(gbs(dl.bytes, ms), 1)}
+        del dl
+        torch.cuda.empty_cache()
+    out["gemm_m2048_8192x8192_k4"] = gemm_rate(torch, ex, "8192_k4", codebook=1)
     return out
 
 
@@ -414,16 +406,138 @@ def encode_rates(torch, ex, n_tiles=2048, Ks=(2, 3, 4)):
     return out
 
 
-def only_mode(what, steps, replicas):
-    """Short runs for the profiler: the fused gate+up launch at K=4 alone (the
-    dominant kernel), the m=2048 8192->8192 K=4 GEMM, or a plain copy of known
-    size."""
+def copy_bandwidth(torch, nbytes=GIB, iters=10):
+    a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out = 2 * nbytes * iters / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    return round(out, 1)
+
+
+# ------------------------------------------------------------ CPU oracle ----
+def _decode_chunk(args):
+    from oracle import exl3_oracle as O
+    words, K = args
+    return O.dequant(words, K)
+
+
+def cpu_baseline(workers=None):
+    """The CPU oracle, as it stands, on a bounded sample of every workload.
+    Decode (the oracle's exact dequantisation, strip blocks spread over all
+    host cores by a process pool) and contraction (the rotation and the
+    float64 product through NumPy's BLAS, all cores) are timed apart; the
+    single 4096x4096 layer also on one core.  Runs before the GPU is touched
+    (the pool forks)."""
+    import multiprocessing as mp
+
+    import synth
+    from oracle import exl3_oracle as O
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    workers = workers or min(cores, 16)
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
+    blas = None
+    if threadpool_info:
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads")} for i in threadpool_info()]
+    pool = mp.get_context("fork").Pool(workers)
+
+    def decode(words, K, strips_per_task=16):
+        tasks = [(words[a:a + strips_per_task], K) for a in range(0, words.shape[0], strips_per_task)]
+        return np.concatenate(pool.map(_decode_chunk, tasks), axis=0)
+
+    def one(mm, strips=None, rows=None):
+        """Decode + contraction seconds of one matmul, on its first `strips`
+        strips and first `rows` rows of x (sample), scaled to the whole."""
+        words, x, sign, scale = synth.draw(mm)
+        s = strips or words.shape[0]
+        r = rows or mm.m
+        w = np.ascontiguousarray(words[:s])
+        t0 = time.perf_counter()
+        W = decode(w, mm.K)
+        t1 = time.perf_counter()
+        xr = O.rotate(x[:r].astype(np.float64), sign.astype(np.float64))
+        y = (xr @ W.astype(np.float64).T) * scale[:16 * s].astype(np.float64)
+        t2 = time.perf_counter()
+        assert np.isfinite(y).all()
+        fs, fr = words.shape[0] / s, mm.m / r
+        return {"decode_s": (t1 - t0) * fs, "contract_s": (t2 - t1) * fs * fr, "bytes": mm.trellis_bytes,
+                "sampled": f"{s} of {words.shape[0]} strips" + (f", {r} of {mm.m} rows" if r != mm.m else "")}
+
+    def total(parts):
+        d = sum(p["decode_s"] for p in parts)
+        c = sum(p["contract_s"] for p in parts)
+        b = sum(p["bytes"] for p in parts)
+        return {"decode_s": round(d, 3), "contract_s": round(c, 3), "gbs": round(b / (d + c) / 1e9, 4)}
+
+    t_start = time.perf_counter()
+    out = {}
+    c1 = synth.single_layer()[0]
+    out["single_4096x4096_k4_m1"] = total([one(c1)])
+    words, x, sign, scale = synth.draw(c1)
+    if threadpool_limits:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.linear(x, words, sign, scale, c1.K)
+            t1 = time.perf_counter()
+        out["single_4096x4096_k4_m1"]["one_core_s"] = round(t1 - t0, 3)
+        out["single_4096x4096_k4_m1"]["one_core_gbs"] = round(c1.trellis_bytes / (t1 - t0) / 1e9, 4)
+    out["mlp_k4_m1"] = total([one(mm) for lc in synth.mlp_launches(4, 1) for mm in lc.members])
+    out["llama70b_gate_k3_m1"] = total([one(synth.llama70b_launches()[1].members[0], strips=224)])
+    g = synth.prefill_gemm()[0]
+    out["gemm_m2048_8192x8192_k4"] = total([one(g, rows=256)])
+    t = out["gemm_m2048_8192x8192_k4"]
+    t["tflops"] = round(2.0 * g.m * g.n_in * g.n_out / (t["decode_s"] + t["contract_s"]) / 1e12, 5)
+    layer0 = synth.llama8b_stack()[:7]
+    part = total([one(mm) for mm in layer0])
+    all_bytes = sum(mm.trellis_bytes for mm in synth.llama8b_stack())
+    l0_bytes = sum(mm.trellis_bytes for mm in layer0)
+    scale_up = all_bytes / l0_bytes
+    stack = {"decode_s": round(part["decode_s"] * scale_up, 2), "contract_s": round(part["contract_s"] * scale_up, 2),
+             "gbs": part["gbs"]}
+    stack["tokens_per_s"] = round(1.0 / (stack["decode_s"] + stack["contract_s"]), 5)
+    out["stack_m1"] = stack
+    pool.close()
+    pool.join()
+    wall = time.perf_counter() - t_start
+    return {"value": stack["gbs"], "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": ("the 32-layer stack at m=1, from its first layer's 7 matmuls scaled by the stack's bytes; "
+                       "decode over a fork pool of %d processes, float64 contraction through NumPy's BLAS; "
+                       "other workloads in per_config (70B gate: 224 of 1792 strips; GEMM: 256 of 2048 rows)"
+                       % workers),
+            "host_cores": cores, "cpu_model": model, "blas": blas, "wall_s": round(wall, 1), "per_config": out}
+
+
+# --------------------------------------------------------------- profiling --
+def only_mode(args):
+    """Short runs for the profiler: one launch shape back to back over >= 1 GiB
+    of weights in rotation (stack:<shape>, mlp<m>:<launch>, 70b:<launch>,
+    single), the whole stack step as graph replays (stack), a GEMM
+    (gemm:8192_k4 | gemm:28672_k3), or a plain copy of known size (copy)."""
     import torch
+
     import decode_gemm_exl3_amd as ex
-    if what == "gemm":
-        tf, ms = gemm_tflops(torch, ex, iters=steps)
-        print(json.dumps({"gemm_m2048_8192x8192_k4": {"launches": steps + 1, "tflops": round(tf, 1)}}), flush=True)
-        return
+    import synth
+    ex.load()
+    what = args.only
+    steps = args.steps
     if what == "copy":
         nbytes = 256 << 20
         a = torch.empty(nbytes // 2, dtype=torch.float16, device="cuda")
@@ -433,109 +547,152 @@ def only_mode(what, steps, replicas):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each": nbytes, "copies": steps}), flush=True)
         return
-    calls = [c for c in build_mlp(torch, ex, 1, Ks=(4,), replicas=replicas) if c["name"] == "gate_up_k4"]
-    for i in range(steps):
-        run_step(ex, calls, i % replicas)
-    torch.cuda.synchronize()
-    print(json.dumps({"launches": {c["name"]: steps for c in calls},
-                      "bytes_per_launch": {c["name"]: c["bytes"] for c in calls}}), flush=True)
+    if what == "stack":
+        r = stack_run(torch, ex, steps, 3)
+        print(json.dumps({"stack": r}), flush=True)
+        return
+    kind, _, name = what.partition(":")
+    if kind == "gemm":
+        r = gemm_rate(torch, ex, name, n=steps)
+        print(json.dumps({f"gemm_{name}": r, "launches": steps + 1}), flush=True)
+        return
+    ws = None
+    if kind == "stack":
+        lc = stack_shapes(stack_launches(True))[name][1]
+    elif kind.startswith("mlp"):
+        m = int(kind[3:] or 1)
+        lc = next(x for x in synth.mlp_launches(int(name.split("_k")[1]), m) if x.name == name)
+        ws = ex.Workspace(14336, 14336, 8, m)
+    elif kind == "70b":
+        lc = next(x for x in synth.llama70b_launches() if x.name == name)
+        ws = ex.Workspace(28672, 28672, 8, 1)
+    elif kind == "single":
+        mm = synth.single_layer()[0]
+        lc = synth.Launch(mm.name, [mm])
+    else:
+        raise SystemExit(f"unknown --only {what}")
+    dl = DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=replicas_for(lc), workspace=ws)
+    ms = time_events(torch, ex, dl, steps)
+    print(json.dumps({"launch": what, "launches": steps + 1, "bytes_per_launch": dl.bytes,
+                      "rotation_bytes": dl.replicas * weight_bytes(lc), "event_us": round(ms * 1e3, 3)}), flush=True)
 
 
+def trace_summary(path, top=12, kernel=None):
+    """Per-kernel count, median, mean, min and max duration (ns) from a
+    rocprofv3 kernel_trace.csv; with `kernel` (a substring of its name) one
+    JSON object for that kernel instead."""
+    import csv
+    durs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            d = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+            durs.setdefault(row["Kernel_Name"], []).append(d)
+    if kernel:
+        name = next(k for k in durs if kernel in k)
+        v = np.asarray(durs[name])
+        print(json.dumps({"kernel": name, "dispatches": int(v.size), "median_ns": int(np.median(v)),
+                          "mean_ns": int(v.mean()), "min_ns": int(v.min()), "max_ns": int(v.max()),
+                          "kernel_sources_hash": kernel_sources_hash()}))
+        return
+    rows = sorted(durs.items(), key=lambda kv: -sum(kv[1]))
+    total = sum(sum(v) for v in durs.values())
+    print("# columns: kernel | calls | median ns | mean ns | min ns | max ns | percent of GPU time")
+    for k, v in rows[:top]:
+        v = np.asarray(v)
+        print(f"{k} | {v.size} | {int(np.median(v))} | {int(v.mean())} | {int(v.min())} | {int(v.max())} | "
+              f"{100.0 * v.sum() / total:.2f}")
+
+
+# -------------------------------------------------------------------- main --
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--replicas", type=int, default=7)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="headline line only (no m=4/8, GEMM, 70B, stack)")
-    ap.add_argument("--only", choices=["gate_up_k4", "gemm", "copy"], help="profiling runs: one launch shape only")
+    ap.add_argument("--no-extra", action="store_true", help="headline, roofline and baseline only")
+    ap.add_argument("--only", help="profiling runs: one launch shape only (see only_mode)")
+    ap.add_argument("--trace-summary", help="summarise a rocprofv3 kernel_trace.csv and exit")
+    ap.add_argument("--trace-kernel", help="with --trace-summary: one kernel (name substring) as JSON")
     args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, kernel=args.trace_kernel)
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        only_mode(args)
+        return
+
+    # the CPU oracle first: its process pool forks before the GPU is touched
+    cpu = None if args.no_cpu else cpu_baseline()
 
     import torch
+
     import decode_gemm_exl3_amd as ex
     ex.load()
     torch.cuda.init()
-    if args.only:
-        only_mode(args.only, args.steps, args.replicas)
-        return
 
-    calls = build_mlp(torch, ex, 1, replicas=args.replicas)
-    step_bytes = sum(c["bytes"] for c in calls)
-    ms, wall = time_graphs(torch, ex, calls, args.replicas, args.steps, args.warmup)
-    value = step_bytes / (ms * 1e-3) / 1e9
+    head = stack_run(torch, ex, args.steps, args.warmup, fused=True)
+    ms = head["ms_per_token"]
+    value = gbs(head["bytes_per_token"], ms)
 
-    kdur = per_kernel_events(torch, ex, calls, args.replicas, max(10, min(args.steps, 50)))
-    launches = {c["name"]: {"us": round(1e3 * kdur[c["name"]], 2),
-                            "gbs": round(c["bytes"] / (kdur[c["name"]] * 1e-3) / 1e9, 1)} for c in calls}
-    per_k = {}
-    for K in (2, 3, 4):
-        sel = [c for c in calls if c["K"] == K]
-        b = sum(c["bytes"] for c in sel)
-        t = sum(kdur[c["name"]] for c in sel)
-        per_k[f"k{K}"] = {"gbs": round(b / (t * 1e-3) / 1e9, 1)}
-    dom = next(c for c in calls if c["name"] == "gate_up_k4")
-    dom_ms = kdur[dom["name"]]
-    achieved = dom["bytes"] / (dom_ms * 1e-3) / 1e9
+    shapes = stack_shape_times(torch, ex)
+    dom_key = max(shapes, key=lambda k: shapes[k]["total_us"])
+    dom = shapes[dom_key]
+    achieved = gbs(dom["bytes_per_launch"], dom["us"] * 1e-3)
+    prof = profile_record(f"stack_{dom_key}_kernel_trace.json")
+    traffic = profile_record(f"stack_{dom_key}_traffic.json")
+    issue = profile_record(f"stack_{dom_key}_issue.json")
+    kernel = f"gemv_kernel<K={dom['K']}> {dom_key}: {dom['n_in']}->{'+'.join(map(str, dom['n_outs']))}, m=1"
+    roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic.get("hbm_bytes_per_launch") if traffic else None,
+                "bytes_per_launch": dom["bytes_per_launch"], "event_us": dom["us"],
+                "share_of_step": dom["share"], "rotation_bytes": dom["rotation_bytes"]}
+    if prof:
+        med = prof["median_ns"] * 1e-6
+        roofline["profile_median_us"] = round(prof["median_ns"] * 1e-3, 3)
+        roofline["profile_frac"] = round(gbs(dom["bytes_per_launch"], med) / HBM_PEAK_GBS, 4)
+    alu = None
+    if issue:
+        n = issue["valu_insts_without_mfma"]
+        a = n * 64 / (dom["us"] * 1e-6)
+        alu = {"bound": "alu", "kernel": kernel, "achieved": round(a / 1e12, 2),
+               "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2), "unit": "T lane-ops/s",
+               "frac": round(a / VALU_PEAK_LANE_OPS, 4), "valu_insts_per_launch": int(n)}
 
-    extra = {"launches_m1": launches, "per_bits_m1": per_k, "copy_gbs": round(copy_bandwidth(torch), 1),
-             "step_bytes": step_bytes, "wall_s": round(wall, 3)}
-    del calls
-    torch.cuda.empty_cache()
+    extra = {"stack_launch_shapes": shapes, "copy_gbs": copy_bandwidth(torch)}
     if not args.no_extra:
-        for m in (4, 8):
-            calls = build_mlp(torch, ex, m, replicas=args.replicas)
-            msm, _ = time_graphs(torch, ex, calls, args.replicas, max(20, args.steps // 4), 5)
-            extra[f"m{m}_gbs"] = round(sum(c["bytes"] for c in calls) / (msm * 1e-3) / 1e9, 1)
-            del calls
-            torch.cuda.empty_cache()
-        tf, gms = gemm_tflops(torch, ex)
-        tfr, rms = fp16_matmul_tflops(torch)
-        extra["gemm_m2048_8192x8192_k4"] = {"tflops": round(tf, 1), "ms": round(gms, 3),
-                                            "frac_of_mfma_f16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                            "plain_fp16_matmul_same_shape": {"tflops": round(tfr, 1),
-                                                                             "ms": round(rms, 3)}}
-        tf3, gms3 = gemm_tflops(torch, ex, n_out=28672, K=3)
-        extra["gemm_m2048_8192x28672_k3"] = {"tflops": round(tf3, 1), "ms": round(gms3, 3),
-                                             "frac_of_mfma_f16_peak": round(tf3 / MFMA_F16_PEAK_TFLOPS, 4)}
+        extra["single_4096x4096_k4_m1"] = single_layer_rate(torch, ex)
+        for m in (1, 4, 8):
+            extra[f"mlp_m{m}"] = mlp_rates(torch, ex, m, max(20, args.steps // 4))
         extra["llama70b_m1"] = llama70b_rates(torch, ex)
+        extra["gemm_m2048_8192x8192_k4"] = gemm_rate(torch, ex, "8192_k4")
+        extra["gemm_m2048_8192x8192_k4"]["plain_fp16_matmul_same_shape"] = fp16_matmul_tflops(torch)
+        extra["gemm_m2048_8192x28672_k3"] = gemm_rate(torch, ex, "28672_k3")
+        extra["medium_m_4096x14336_k4"] = medium_m_rates(torch, ex)
+        extra["codebook1"] = codebook1_rates(torch, ex)
         extra["encode"] = encode_rates(torch, ex)
-        extra["medium_m_4096x14336_k4"] = medium_m(torch, ex)
-        # the byte-sum (dp4a) codebook on the K=4 MLP launches and the GEMM
-        calls = build_mlp(torch, ex, 1, Ks=(4,), replicas=args.replicas)
-        for c in calls:
-            c["codebook"] = 1
-        kd1 = per_kernel_events(torch, ex, calls, args.replicas, 20)
-        tf1, gms1 = gemm_tflops(torch, ex, codebook=1)
-        extra["codebook1"] = {c["name"]: {"us": round(1e3 * kd1[c["name"]], 2),
-                                          "gbs": round(c["bytes"] / (kd1[c["name"]] * 1e-3) / 1e9, 1)} for c in calls}
-        extra["codebook1"]["gemm_m2048_8192x8192_k4"] = {"tflops": round(tf1, 1), "ms": round(gms1, 3)}
-        del calls
-        torch.cuda.empty_cache()
-        extra["llama8b_stack_m1"] = {"fused": stack_tokens_per_s(torch, ex, True),
-                                     "unfused": stack_tokens_per_s(torch, ex, False)}
+        extra["stack_unfused"] = stack_run(torch, ex, max(20, args.steps // 4), 3, fused=False)
 
     rec = {
-        "metric": "EXL3 GEMV achieved HBM GB/s at m=1 (Llama-3.1-8B MLP, K=2,3,4)",
+        "metric": "EXL3 GEMV achieved HBM GB/s at m=1 (32-layer Llama-3.1-8B-shaped stack, 224 matmuls)",
         "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": "llama3.1-8b-mlp-gemv: gate/up 4096->14336 (one fused launch), down 14336->4096, "
-                               "K in {2,3,4}, m=1, 6 launches (9 projections) per step",
-                   "m": 1, "bits": [2, 3, 4], "weight_replicas": args.replicas},
-        "roofline": {"bound": "hbm", "kernel": "gemv_kernel<K=4> gate+up 4096->2x14336",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic()},
+        "config": {"workload": "llama3.1-8b-shaped 32-layer linear stack at m=1: q 4096->4096, k/v 4096->1024, "
+                               "o 4096->4096, gate/up 4096->14336, down 14336->4096 per layer, K_b from {2..6} "
+                               "(attention +1), q/k/v and gate/up fused, 128 launches per token as one HIP graph",
+                   "m": 1, "tokens_per_s": head["tokens_per_s"], "bytes_per_token": head["bytes_per_token"]},
+        "roofline": roofline,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "alu_roofline": alu_roofline(dom_ms),
+        "alu_roofline": alu,
         "extra": extra,
     }
-    if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 
