@@ -223,13 +223,18 @@ def stack_shape_times(torch, ex, n=50):
 
 
 # -------------------------------------------------------------- profiles ----
-def kernel_sources_hash() -> str:
-    """Hash of the GEMV kernel and launch-plan sources with comments and blank
-    lines removed: profile-derived figures are valid only for this code."""
+GEMV_SOURCES = ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip")
+GEMM_SOURCES = ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip", "exl3_gemm.hip")
+
+
+def kernel_sources_hash(files=GEMV_SOURCES) -> str:
+    """Hash of the kernel and launch-plan sources (the GEMV's by default, the
+    GEMM's with its rotation pre-pass otherwise) with comments and blank lines
+    removed: profile-derived figures are valid only for this code."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip"):
+    for f in files:
         with open(os.path.join(ROOT, "decode_gemm_exl3_amd", "csrc", f), encoding="utf-8") as fh:
             text = fh.read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -505,7 +510,7 @@ def cpu_baseline(workers=None):
     out["gemm_m2048_8192x8192_k4"] = total([one(g, rows=256)])
     t = out["gemm_m2048_8192x8192_k4"]
     t["tflops"] = round(2.0 * g.m * g.n_in * g.n_out / (t["decode_s"] + t["contract_s"]) / 1e12, 5)
-    layer0 = synth.llama8b_stack()[:7]
+    layer0 = synth.llama8b_stack()[:4 * 7]  # the first four layers
     part = total([one(mm) for mm in layer0])
     all_bytes = sum(mm.trellis_bytes for mm in synth.llama8b_stack())
     l0_bytes = sum(mm.trellis_bytes for mm in layer0)
@@ -518,7 +523,7 @@ def cpu_baseline(workers=None):
     pool.join()
     wall = time.perf_counter() - t_start
     return {"value": stack["gbs"], "unit": "GB/s", "cores": workers, "kind": "oracle",
-            "sample": ("the 32-layer stack at m=1, from its first layer's 7 matmuls scaled by the stack's bytes; "
+            "sample": ("the 32-layer stack at m=1, from its first four layers' 28 matmuls scaled by the stack's bytes; "
                        "decode over a fork pool of %d processes, float64 contraction through NumPy's BLAS; "
                        "other workloads in per_config (70B gate: 224 of 1792 strips; GEMM: 256 of 2048 rows)"
                        % workers),
@@ -551,26 +556,21 @@ def only_mode(args):
         r = stack_run(torch, ex, steps, 3)
         print(json.dumps({"stack": r}), flush=True)
         return
+    if what == "fp16mm":
+        r = fp16_matmul_tflops(torch, iters=steps)
+        print(json.dumps({"plain_fp16_matmul_2048x8192x8192": r, "launches": steps + 1}), flush=True)
+        return
     kind, _, name = what.partition(":")
     if kind == "gemm":
         r = gemm_rate(torch, ex, name, n=steps)
         print(json.dumps({f"gemm_{name}": r, "launches": steps + 1}), flush=True)
         return
+    lc = _spec_launch(what)
     ws = None
-    if kind == "stack":
-        lc = stack_shapes(stack_launches(True))[name][1]
-    elif kind.startswith("mlp"):
-        m = int(kind[3:] or 1)
-        lc = next(x for x in synth.mlp_launches(int(name.split("_k")[1]), m) if x.name == name)
-        ws = ex.Workspace(14336, 14336, 8, m)
+    if kind.startswith("mlp"):
+        ws = ex.Workspace(14336, 14336, 8, lc.m)
     elif kind == "70b":
-        lc = next(x for x in synth.llama70b_launches() if x.name == name)
         ws = ex.Workspace(28672, 28672, 8, 1)
-    elif kind == "single":
-        mm = synth.single_layer()[0]
-        lc = synth.Launch(mm.name, [mm])
-    else:
-        raise SystemExit(f"unknown --only {what}")
     dl = DevLaunch(torch, ex, lc, gemv_fn(lc), replicas=replicas_for(lc), workspace=ws)
     ms = time_events(torch, ex, dl, steps)
     print(json.dumps({"launch": what, "launches": steps + 1, "bytes_per_launch": dl.bytes,
@@ -603,6 +603,136 @@ def trace_summary(path, top=12, kernel=None):
               f"{100.0 * v.sum() / total:.2f}")
 
 
+def _median_counters(path, kernel):
+    """Median over the dispatches of `kernel` of every counter in a rocprofv3
+    counter_collection.csv."""
+    import csv
+    vals = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row["Kernel_Name"] == kernel:
+                vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    return {k: float(np.median(v)) for k, v in vals.items()}, max((len(v) for v in vals.values()), default=0)
+
+
+SQ_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
+               "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
+
+
+def make_profile(prof_dir, tag, spec):
+    """The committed profile summary of one launch shape (JSON on stdout) from
+    the rocprofv3 outputs of the passes listed under "commands": the kernel
+    trace (durations), FETCH_SIZE and WRITE_SIZE (HBM traffic, scaled by what
+    the same counters read for a plain 256 MiB device copy) and the SQ and GRBM
+    counters (instructions, matrix-core busy cycles, clock)."""
+    import csv
+    trace = os.path.join(prof_dir, f"{tag}_trace_kernel_trace.csv")
+    durs = {}
+    with open(trace) as f:
+        for row in csv.DictReader(f):
+            if "exl3::" in row["Kernel_Name"] or (spec == "fp16mm" and "Cijk" in row["Kernel_Name"]):
+                durs.setdefault(row["Kernel_Name"], []).append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    kernel = max(durs, key=lambda k: sum(durs[k]))
+    v = np.asarray(durs[kernel])
+    is_gemm = spec.startswith("gemm:") or spec == "fp16mm"
+    rec = {"launch": spec, "kernel": kernel, "kernel_sources_hash": kernel_sources_hash(GEMM_SOURCES if is_gemm else
+                                                                                        GEMV_SOURCES),
+           "dispatches": int(v.size),
+           "median_ns": int(np.median(v)), "mean_ns": int(v.mean()), "min_ns": int(v.min()), "max_ns": int(v.max())}
+    others = {k: {"dispatches": len(d), "median_ns": int(np.median(d))} for k, d in durs.items() if k != kernel}
+    if others:
+        rec["other_kernels"] = others
+    med_s = rec["median_ns"] * 1e-9
+    if is_gemm:
+        import synth
+        mm = synth.prefill_gemm()[0 if spec in ("gemm:8192_k4", "fp16mm") else 1]
+        flops = 2.0 * mm.m * mm.n_in * mm.n_out
+        rec["workload"] = (f"prefill GEMM m={mm.m}, {mm.n_in}->{mm.n_out}, K={mm.K}" if spec != "fp16mm" else
+                           "plain fp16 matrix product 2048x8192 by 8192x8192 through torch's BLAS (no decode)")
+        rec["flops"] = flops
+        rec["median_tflops"] = round(flops / med_s / 1e12, 1)
+        rec["frac_of_mfma_f16_peak"] = round(flops / med_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)
+    else:
+        lc = _spec_launch(spec)
+        b = launch_bytes(lc)
+        rec["workload"] = f"{lc.name}: {lc.n_in}->{'+'.join(map(str, lc.n_outs))}, K={lc.K}, m={lc.m}"
+        rec["algorithmic_bytes_per_launch"] = b
+        rec["median_gbs"] = round(b / med_s / 1e9, 1)
+        rec["frac_of_hbm_peak"] = round(b / med_s / 1e9 / HBM_PEAK_GBS, 4)
+    fpath = os.path.join(prof_dir, f"{tag}_fetch_counter_collection.csv")
+    if os.path.exists(fpath):
+        cf, _ = _median_counters(os.path.join(prof_dir, "copy_fetch_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+        cw, _ = _median_counters(os.path.join(prof_dir, "copy_write_counter_collection.csv"), "__amd_rocclr_copyBuffer")
+        copy_bytes = 256 << 20
+        fs = copy_bytes / (cf["FETCH_SIZE"] * 1024)
+        ws = copy_bytes / (cw["WRITE_SIZE"] * 1024)
+        kf, nf = _median_counters(fpath, kernel)
+        kw, _ = _median_counters(os.path.join(prof_dir, f"{tag}_write_counter_collection.csv"), kernel)
+        hbm = kf["FETCH_SIZE"] * 1024 * fs + kw["WRITE_SIZE"] * 1024 * ws
+        rec["traffic"] = {"fetch_size_kib_median": kf["FETCH_SIZE"], "write_size_kib_median": kw["WRITE_SIZE"],
+                          "dispatches": nf, "copy_fetch_scale": round(fs, 4), "copy_write_scale": round(ws, 4),
+                          "hbm_bytes_per_launch": int(hbm),
+                          "traffic_over_algorithmic": round(hbm / rec.get("algorithmic_bytes_per_launch", hbm), 4)}
+    qpath = os.path.join(prof_dir, f"{tag}_sq_counter_collection.csv")
+    if os.path.exists(qpath):
+        q, nq = _median_counters(qpath, kernel)
+        valu = q["SQ_INSTS_VALU"] - q["SQ_INSTS_MFMA"]  # SQ_INSTS_VALU counts the MFMAs too
+        se_cycles = q["SQ_BUSY_CYCLES"] / 32           # summed over the 32 shader engines
+        clock = se_cycles / med_s                        # shader clock while the kernel ran (a lower bound)
+        mfma_cycles = q["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
+        rec["issue"] = {"dispatches": nq, "sq_insts_valu": q["SQ_INSTS_VALU"], "sq_insts_mfma": q["SQ_INSTS_MFMA"],
+                        "sq_insts_salu": q["SQ_INSTS_SALU"], "valu_insts_without_mfma": valu,
+                        "mfma_busy_cycles_per_simd": mfma_cycles,
+                        "valu_coexec_frac_of_mfma_busy": round(q["SQ_VALU_MFMA_COEXEC_CYCLES"]
+                                                               / max(q["SQ_VALU_MFMA_BUSY_CYCLES"], 1), 4),
+                        "sq_busy_cycles_per_se": se_cycles, "grbm_gui_active": q["GRBM_GUI_ACTIVE"],
+                        "clock_ghz_est": round(clock / 1e9, 3),
+                        "mfma_busy_frac_at_est_clock": round(mfma_cycles / se_cycles, 4),
+                        "valu_lane_ops_per_s": valu * 64 / med_s,
+                        "valu_frac_of_issue_peak": round(valu * 64 / med_s / VALU_PEAK_LANE_OPS, 4)}
+        if "flops" in rec:
+            peak_at_clock = MFMA_F16_PEAK_TFLOPS * (clock / 2.4e9)
+            rec["issue"]["mfma_f16_peak_at_est_clock_tflops"] = round(peak_at_clock, 1)
+            rec["issue"]["frac_of_peak_at_est_clock"] = round(rec["median_tflops"] / peak_at_clock, 4)
+    cmds = [f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o {tag}_trace -- "
+            f"python3 <repo>/bench.py --only {spec} --steps {30 if is_gemm else 60}"]
+    if os.path.exists(fpath):
+        cmds += [f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o {tag}_fetch -- "
+                 f"python3 <repo>/bench.py --only {spec} --steps 20",
+                 f"cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d <out> -o {tag}_write -- "
+                 f"python3 <repo>/bench.py --only {spec} --steps 20",
+                 "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o copy_fetch -- "
+                 "python3 <repo>/bench.py --only copy --steps 20   (and WRITE_SIZE into copy_write)"]
+    if os.path.exists(qpath):
+        cmds.append(f"cd /tmp && rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d <out> -o {tag}_sq -- "
+                    f"python3 <repo>/bench.py --only {spec} --steps {10 if is_gemm else 20}")
+    cmds.append(f"python3 <repo>/bench.py --make-profile {tag} --prof-dir <out> --only {spec}")
+    rec["commands"] = cmds
+    rec["derivation"] = ("durations: End - Start of the kernel's dispatches in the trace; traffic: FETCH_SIZE and "
+                         "WRITE_SIZE medians (KiB) times the bytes a 256 MiB copy moves over what the same counter "
+                         "reads for it; SQ_INSTS_VALU counts MFMAs, so vector instructions = SQ_INSTS_VALU - "
+                         "SQ_INSTS_MFMA (64 lane-operations each); SQ_BUSY_CYCLES is read as summed over the 32 "
+                         "shader engines, so SQ_BUSY_CYCLES / 32 / median duration estimates the shader clock the "
+                         "kernel ran at (a lower bound: cycles with no wave resident do not count); MFMA busy "
+                         "fraction = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (SQ_BUSY_CYCLES / 32)")
+    print(json.dumps(rec, indent=1))
+
+
+def _spec_launch(spec):
+    import synth
+    kind, _, name = spec.partition(":")
+    if kind == "stack":
+        return stack_shapes(stack_launches(True))[name][1]
+    if kind.startswith("mlp"):
+        return next(x for x in synth.mlp_launches(int(name.split("_k")[1]), int(kind[3:] or 1)) if x.name == name)
+    if kind == "70b":
+        return next(x for x in synth.llama70b_launches() if x.name == name)
+    if kind == "single":
+        mm = synth.single_layer()[0]
+        return synth.Launch(mm.name, [mm])
+    raise SystemExit(f"unknown launch {spec}")
+
+
 # -------------------------------------------------------------------- main --
 def main():
     ap = argparse.ArgumentParser()
@@ -614,7 +744,12 @@ def main():
     ap.add_argument("--only", help="profiling runs: one launch shape only (see only_mode)")
     ap.add_argument("--trace-summary", help="summarise a rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--trace-kernel", help="with --trace-summary: one kernel (name substring) as JSON")
+    ap.add_argument("--make-profile", help="profile summary of a launch shape (tag of the rocprofv3 outputs)")
+    ap.add_argument("--prof-dir", help="with --make-profile: the rocprofv3 output folder")
     args = ap.parse_args()
+    if args.make_profile:
+        make_profile(args.prof_dir, args.make_profile, args.only)
+        return
     if args.trace_summary:
         trace_summary(args.trace_summary, kernel=args.trace_kernel)
         return
@@ -642,9 +777,9 @@ def main():
     dom_key = max(shapes, key=lambda k: shapes[k]["total_us"])
     dom = shapes[dom_key]
     achieved = gbs(dom["bytes_per_launch"], dom["us"] * 1e-3)
-    prof = profile_record(f"stack_{dom_key}_kernel_trace.json")
-    traffic = profile_record(f"stack_{dom_key}_traffic.json")
-    issue = profile_record(f"stack_{dom_key}_issue.json")
+    prof = profile_record(f"gemv_stack8b_{dom_key}.json")
+    traffic = prof.get("traffic") if prof else None
+    issue = prof.get("issue") if prof else None
     kernel = f"gemv_kernel<K={dom['K']}> {dom_key}: {dom['n_in']}->{'+'.join(map(str, dom['n_outs']))}, m=1"
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
