@@ -462,3 +462,60 @@ def test_linear_dispatch(torch_cuda):
         words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [19, n_in, m])
         y = run_linear(torch_cuda, "linear", words, x, sign, scale, K)
         assert_close(y, O.linear(x, words, sign, scale, K), (n_in, n_out, K, m))
+
+
+# ------------------------------------------------------------- edge cases ----
+def test_degenerate_inputs(torch_cuda):
+    # x = 0 and out_scale = 0 give exactly zero on every path; inputs near the
+    # top of the fp16 range do not overflow the rotated input (x'/128 is never
+    # larger than max|x|), checked against the oracle with a small scale
+    for fn, m in (("gemv", 1), ("gemv", 5), ("gemm", 40), ("gemm", 300)):
+        words, x, sign, scale = synth.random_case(1024, 272, 3, m, [71, m])
+        log(f"degenerate {fn} m={m}")
+        y = run_linear(torch_cuda, fn, words, np.zeros_like(x), sign, scale, 3)
+        assert (y.view(np.uint16) & 0x7FFF == 0).all()
+        y = run_linear(torch_cuda, fn, words, x, sign, np.zeros_like(scale), 3)
+        assert (y.view(np.uint16) & 0x7FFF == 0).all()
+        big = (np.sign(x.astype(np.float32)) * 60000).astype(np.float16)  # all-same-magnitude, worst case for x'
+        tiny = np.full_like(scale, 1e-4)
+        y = run_linear(torch_cuda, fn, words, big, sign, tiny, 3)
+        assert_close(y, O.linear(big, words, sign, tiny, 3), (fn, m, "large inputs"))
+
+
+def test_largest_weight_matrix(torch_cuda):
+    # the largest weight one call takes at K = 8 (32768 x 65488, just under the
+    # 2^31 - 2^20 bytes read through 32-bit offsets), one output per strip
+    # compared; one more strip is refused
+    import decode_gemm_exl3_amd as ex
+    n_in, n_out, K = 32768, 65488, 8
+    assert n_in * n_out * K // 8 < (1 << 31) - (1 << 20) <= n_in * (n_out + 16) * K // 8
+    log(f"largest weight {n_in}x{n_out} K={K}")
+    words, x, sign, scale = synth.random_case(n_in, n_out, K, 1, [73])
+    y = run_linear(torch_cuda, "gemv", words, x, sign, scale, K)
+    rows = strip_rows(n_out, np.random.default_rng(73))
+    assert_close(y[:, rows], O.linear_rows(x, words, sign, scale, K, rows), "largest weight")
+    lib = ex.load()
+    A = 1 << 20
+    assert lib.exl3_gemv(A, 1, A, A, A, n_in, n_out + 16, K, A + 64, None, 0, None) == -2
+
+
+def test_gemm_largest_m(torch_cuda):
+    # the most rows the GEMM takes at n_in = 8192 (130816: the rotated input
+    # just under 2^31 - 2^20 bytes), sampled rows of the output compared; one
+    # more block of rows is refused
+    import decode_gemm_exl3_amd as ex
+    torch = torch_cuda
+    n_in, n_out, K, m = 8192, 16, 4, 130816
+    log(f"gemm largest m={m} n_in={n_in}")
+    words, _, sign, scale = synth.random_case(n_in, n_out, K, 1, [74])
+    x = torch.randn((m, n_in), device="cuda").half()
+    ws = ex.Workspace(n_in, n_out, K, m)
+    y = ex.gemm(x, to_dev(torch, words), to_dev(torch, sign), to_dev(torch, scale), K, workspace=ws)
+    torch.cuda.synchronize()
+    sel = np.unique(np.concatenate([np.arange(64), m - 64 + np.arange(64),
+                                    np.random.default_rng(74).integers(0, m, 256)]))
+    xs = x[torch.from_numpy(sel).cuda()].cpu().numpy()
+    assert_close(y[torch.from_numpy(sel).cuda()].cpu().numpy(), O.linear(xs, words, sign, scale, K), "largest m")
+    lib = ex.load()
+    A = 1 << 20
+    assert lib.exl3_gemm(A, m + 256, A, A, A, n_in, n_out, K, A + 64, A + 128, 1 << 40, None) == -2

@@ -67,3 +67,29 @@ def test_noalloc_matches_linear(torch_cuda, seq):
         a, b = y_na.cpu().numpy(), y_ref.cpu().numpy()
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (seq, call)
         assert rel_fro(a, O.linear(x, words, sign, scale, K)) <= TOL, (seq, call)
+
+
+def test_noalloc_at_its_limit(torch_cuda):
+    # 4096 rows of 8192 inputs: the rotated input fills the 64 MiB scratch
+    # exactly, so the input dimension is not split; exl3_linear given a
+    # workspace of the same 64 MiB takes the same plan and gives the same bits
+    import decode_gemm_exl3_amd as ex
+    torch = torch_cuda
+    n_in, n_out, K, m = 8192, 32, 2, 4096
+    print(f"[case] noalloc at the limit n_in={n_in} n_out={n_out} K={K} m={m}", flush=True)
+    words, _, sign, scale = synth.random_case(n_in, n_out, K, 1, [62])
+    x = torch.randn((m, n_in), device="cuda").half()
+    d = [x] + [to_dev(torch, a) for a in (words, sign, scale)]
+    y_na = torch.full((m, n_out), float("nan"), dtype=torch.float16, device="cuda")
+    ex.linear_noalloc(*d, K, y=y_na)
+
+    class Ws:  # a workspace of exactly the scratch's size
+        buf = torch.empty(SCRATCH, dtype=torch.uint8, device="cuda")
+        nbytes = SCRATCH
+
+    y_ref = ex.linear(*d, K, workspace=Ws())
+    torch.cuda.synchronize()
+    assert torch.equal(y_na.view(torch.int16), y_ref.view(torch.int16))
+    sel = np.unique(np.concatenate([np.arange(8), m - 8 + np.arange(8), np.random.default_rng(62).integers(0, m, 48)]))
+    selt = torch.from_numpy(sel).cuda()
+    assert rel_fro(y_na[selt].cpu().numpy(), O.linear(x[selt].cpu().numpy(), words, sign, scale, K)) <= TOL
