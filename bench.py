@@ -615,6 +615,8 @@ def _median_counters(path, kernel):
     return {k: float(np.median(v)) for k, v in vals.items()}, max((len(v) for v in vals.values()), default=0)
 
 
+STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+                  "SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS")
 SQ_COUNTERS = ("SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES "
                "SQ_BUSY_CYCLES GRBM_GUI_ACTIVE")
 
@@ -694,6 +696,15 @@ def make_profile(prof_dir, tag, spec):
             peak_at_clock = MFMA_F16_PEAK_TFLOPS * (clock / 2.4e9)
             rec["issue"]["mfma_f16_peak_at_est_clock_tflops"] = round(peak_at_clock, 1)
             rec["issue"]["frac_of_peak_at_est_clock"] = round(rec["median_tflops"] / peak_at_clock, 4)
+    spath = os.path.join(prof_dir, f"{tag}_stall_counter_collection.csv")
+    if os.path.exists(spath):
+        q, ns = _median_counters(spath, kernel)
+        wc = max(q["SQ_WAVE_CYCLES"], 1)
+        rec["stalls"] = {"dispatches": ns, **{k.lower(): q[k] for k in sorted(q)},
+                         "wait_any_frac_of_wave_cycles": round(q["SQ_WAIT_ANY"] / wc, 4),
+                         "wait_inst_any_frac_of_wave_cycles": round(q["SQ_WAIT_INST_ANY"] / wc, 4),
+                         "lds_bank_conflict_frac_of_lds_active": round(q["SQ_LDS_BANK_CONFLICT"]
+                                                                       / max(q["SQ_ACTIVE_INST_LDS"], 1), 4)}
     cmds = [f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o {tag}_trace -- "
             f"python3 <repo>/bench.py --only {spec} --steps {30 if is_gemm else 60}"]
     if os.path.exists(fpath):
@@ -706,6 +717,9 @@ def make_profile(prof_dir, tag, spec):
     if os.path.exists(qpath):
         cmds.append(f"cd /tmp && rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d <out> -o {tag}_sq -- "
                     f"python3 <repo>/bench.py --only {spec} --steps {10 if is_gemm else 20}")
+    if os.path.exists(spath):
+        cmds.append(f"cd /tmp && rocprofv3 --pmc {STALL_COUNTERS} --output-format csv -d <out> -o {tag}_stall -- "
+                    f"python3 <repo>/bench.py --only {spec} --steps 10")
     cmds.append(f"python3 <repo>/bench.py --make-profile {tag} --prof-dir <out> --only {spec}")
     rec["commands"] = cmds
     rec["derivation"] = ("durations: End - Start of the kernel's dispatches in the trace; traffic: FETCH_SIZE and "
