@@ -556,6 +556,11 @@ def only_mode(args):
         r = stack_run(torch, ex, steps, 3)
         print(json.dumps({"stack": r}), flush=True)
         return
+    if what.startswith("encode:"):
+        K = int(what.split(":")[1])
+        r = encode_rates(torch, ex, Ks=(K,))
+        print(json.dumps({"encode": r}), flush=True)
+        return
     if what == "fp16mm":
         r = fp16_matmul_tflops(torch, iters=steps)
         print(json.dumps({"plain_fp16_matmul_2048x8192x8192": r, "launches": steps + 1}), flush=True)

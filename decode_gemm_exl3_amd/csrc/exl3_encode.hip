@@ -47,7 +47,13 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
     // block minima, double-buffered where LDS allows (step i writes buffer
     // i & 1, so a step needs one barrier); K = 1 has one buffer and two barriers
     constexpr int NMB = K >= 2 ? 2 : 1;
-    __shared__ float Mbuf[NMB][U];
+    // M is stored with four floats of padding after every 64 entries: the cost
+    // update has each thread read 64 consecutive entries starting at a multiple
+    // of 64, and unpadded every lane of a wave would read the same four banks
+    // (a 64-way conflict on every read of every step)
+    constexpr int MP = U + 4 * (U / 64);
+    auto mpad = [](int u) { return u + 4 * (u >> 6); };
+    __shared__ float Mbuf[NMB][MP];
     __shared__ float wt[256];
     __shared__ uint16_t path[256];
     __shared__ float red_c[ENC_THREADS / 64];
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
 #pragma unroll
                     for (int j = 1; j < BLK; ++j)
                         if (cost[b * BLK + j] < best) { best = cost[b * BLK + j]; bj = j; }
-                    M[(s0 >> K) + b] = best;
+                    M[mpad((s0 >> K) + b)] = best;
                     pk[b >> 2] |= (uint32_t)bj << (8 * (b & 3));
                     // one block at a time: interleaving the independent chains
                     // would hold one comparison mask per element (a tree of
@@ -160,18 +166,19 @@ __global__ __launch_bounds__(ENC_THREADS) void encode_kernel(EncodeParams p) {
                 }
                 if ((tid & ((BLK / ENC_STATES) - 1)) == 0) {
                     const int u = s0 >> K;
-                    M[u] = best;
+                    M[mpad(u)] = best;
                     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)bj, rback, (uint32_t)(i * U + u), 0u, 0);
                 }
             }
             __syncthreads();
             // ---- new costs: M of each state's predecessor block plus its error
             const float wi = wt[(i + rot) & 255];
-            const int u0 = s0 & LOW;  // the thread's 64 states map to u0 .. u0 + 63
+            const int u0 = s0 & LOW;  // the thread's 64 states map to u0 .. u0 + 63 (one padded row)
+            const float* Mrow = M + mpad(u0);
             uint32_t pk = pb;
 #pragma unroll
             for (int k = 0; k < ENC_STATES; k += 4) {
-                const float4 m4 = *reinterpret_cast<const float4*>(&M[u0 + k]);
+                const float4 m4 = *reinterpret_cast<const float4*>(&Mrow[k]);
                 const float mk[4] = {m4.x, m4.y, m4.z, m4.w};
 #pragma unroll
                 for (int e = 0; e < 4; ++e, pk += CA) {
