@@ -225,6 +225,7 @@ def stack_shape_times(torch, ex, n=50):
 # -------------------------------------------------------------- profiles ----
 GEMV_SOURCES = ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip")
 GEMM_SOURCES = ("exl3_device.hpp", "exl3_internal.hpp", "exl3_kernels.hip", "exl3_api.hip", "exl3_gemm.hip")
+ENCODE_SOURCES = ("exl3_device.hpp", "exl3_internal.hpp", "exl3_api.hip", "exl3_encode.hip")
 
 
 def kernel_sources_hash(files=GEMV_SOURCES) -> str:
@@ -608,16 +609,18 @@ def trace_summary(path, top=12, kernel=None):
               f"{100.0 * v.sum() / total:.2f}")
 
 
-def _median_counters(path, kernel):
+def _median_counters(path, kernel, largest=False):
     """Median over the dispatches of `kernel` of every counter in a rocprofv3
-    counter_collection.csv."""
+    counter_collection.csv (with `largest`, the largest value instead: the
+    timed launch of a run whose warm-up launch is smaller)."""
     import csv
     vals = {}
     with open(path) as f:
         for row in csv.DictReader(f):
             if row["Kernel_Name"] == kernel:
                 vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
-    return {k: float(np.median(v)) for k, v in vals.items()}, max((len(v) for v in vals.values()), default=0)
+    pick = (lambda v: float(np.max(v))) if largest else (lambda v: float(np.median(v)))
+    return {k: pick(v) for k, v in vals.items()}, max((len(v) for v in vals.values()), default=0)
 
 
 STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
@@ -642,15 +645,22 @@ def make_profile(prof_dir, tag, spec):
     kernel = max(durs, key=lambda k: sum(durs[k]))
     v = np.asarray(durs[kernel])
     is_gemm = spec.startswith("gemm:") or spec == "fp16mm"
-    rec = {"launch": spec, "kernel": kernel, "kernel_sources_hash": kernel_sources_hash(GEMM_SOURCES if is_gemm else
-                                                                                        GEMV_SOURCES),
+    files = GEMM_SOURCES if is_gemm else (ENCODE_SOURCES if spec.startswith("encode:") else GEMV_SOURCES)
+    rec = {"launch": spec, "kernel": kernel, "kernel_sources_hash": kernel_sources_hash(files),
            "dispatches": int(v.size),
            "median_ns": int(np.median(v)), "mean_ns": int(v.mean()), "min_ns": int(v.min()), "max_ns": int(v.max())}
     others = {k: {"dispatches": len(d), "median_ns": int(np.median(d))} for k, d in durs.items() if k != kernel}
     if others:
         rec["other_kernels"] = others
     med_s = rec["median_ns"] * 1e-9
-    if is_gemm:
+    if spec.startswith("encode:"):
+        # one warm-up launch of 64 tiles, then the timed launch of 2048 tiles
+        longest = int(v.max())
+        rec["workload"] = f"tail-biting Viterbi encoder, K={spec.split(':')[1]}, 2048 unit-Gaussian tiles"
+        rec["timed_launch_ns"] = longest
+        rec["tiles_per_s"] = round(2048 / (longest * 1e-9))
+        med_s = longest * 1e-9
+    elif is_gemm:
         import synth
         mm = synth.prefill_gemm()[0 if spec in ("gemm:8192_k4", "fp16mm") else 1]
         flops = 2.0 * mm.m * mm.n_in * mm.n_out
@@ -682,7 +692,7 @@ def make_profile(prof_dir, tag, spec):
                           "traffic_over_algorithmic": round(hbm / rec.get("algorithmic_bytes_per_launch", hbm), 4)}
     qpath = os.path.join(prof_dir, f"{tag}_sq_counter_collection.csv")
     if os.path.exists(qpath):
-        q, nq = _median_counters(qpath, kernel)
+        q, nq = _median_counters(qpath, kernel, largest=spec.startswith("encode:"))
         valu = q["SQ_INSTS_VALU"] - q["SQ_INSTS_MFMA"]  # SQ_INSTS_VALU counts the MFMAs too
         se_cycles = q["SQ_BUSY_CYCLES"] / 32           # summed over the 32 shader engines
         clock = se_cycles / med_s                        # shader clock while the kernel ran (a lower bound)
@@ -703,15 +713,16 @@ def make_profile(prof_dir, tag, spec):
             rec["issue"]["frac_of_peak_at_est_clock"] = round(rec["median_tflops"] / peak_at_clock, 4)
     spath = os.path.join(prof_dir, f"{tag}_stall_counter_collection.csv")
     if os.path.exists(spath):
-        q, ns = _median_counters(spath, kernel)
+        q, ns = _median_counters(spath, kernel, largest=spec.startswith("encode:"))
         wc = max(q["SQ_WAVE_CYCLES"], 1)
         rec["stalls"] = {"dispatches": ns, **{k.lower(): q[k] for k in sorted(q)},
                          "wait_any_frac_of_wave_cycles": round(q["SQ_WAIT_ANY"] / wc, 4),
                          "wait_inst_any_frac_of_wave_cycles": round(q["SQ_WAIT_INST_ANY"] / wc, 4),
                          "lds_bank_conflict_frac_of_lds_active": round(q["SQ_LDS_BANK_CONFLICT"]
                                                                        / max(q["SQ_ACTIVE_INST_LDS"], 1), 4)}
+    nsteps = 1 if spec.startswith("encode:") else (30 if is_gemm else 60)
     cmds = [f"cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o {tag}_trace -- "
-            f"python3 <repo>/bench.py --only {spec} --steps {30 if is_gemm else 60}"]
+            f"python3 <repo>/bench.py --only {spec} --steps {nsteps}"]
     if os.path.exists(fpath):
         cmds += [f"cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d <out> -o {tag}_fetch -- "
                  f"python3 <repo>/bench.py --only {spec} --steps 20",
@@ -721,10 +732,10 @@ def make_profile(prof_dir, tag, spec):
                  "python3 <repo>/bench.py --only copy --steps 20   (and WRITE_SIZE into copy_write)"]
     if os.path.exists(qpath):
         cmds.append(f"cd /tmp && rocprofv3 --pmc {SQ_COUNTERS} --output-format csv -d <out> -o {tag}_sq -- "
-                    f"python3 <repo>/bench.py --only {spec} --steps {10 if is_gemm else 20}")
+                    f"python3 <repo>/bench.py --only {spec} --steps {nsteps if nsteps == 1 else (10 if is_gemm else 20)}")
     if os.path.exists(spath):
         cmds.append(f"cd /tmp && rocprofv3 --pmc {STALL_COUNTERS} --output-format csv -d <out> -o {tag}_stall -- "
-                    f"python3 <repo>/bench.py --only {spec} --steps 10")
+                    f"python3 <repo>/bench.py --only {spec} --steps {1 if nsteps == 1 else 10}")
     cmds.append(f"python3 <repo>/bench.py --make-profile {tag} --prof-dir <out> --only {spec}")
     rec["commands"] = cmds
     rec["derivation"] = ("durations: End - Start of the kernel's dispatches in the trace; traffic: FETCH_SIZE and "
