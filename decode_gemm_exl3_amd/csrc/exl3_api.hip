@@ -71,8 +71,6 @@ bool linear_uses_gemv(int32_t m, int32_t n_in) {
     return m <= GEMV_LINEAR_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
 }
 
-// Input length from which a GEMV of 2..8 rows with enough workspace rotates its input in a pre-pass.
-constexpr int GEMV_PREROT_MIN_N_IN = 12288;
 
 // Workspace needs.  Nothing in the workspace survives between calls, so each
 // call lays out only what it uses from offset 0:
@@ -194,13 +192,21 @@ bool plan_gemv(exl3::GemvParams* p) {
 // rather than in every workgroup.  Each workgroup's rotation costs vector
 // issue in proportion to m * n_in; the pre-pass costs one more launch and a
 // copy of the rotated rows from L2 into every workgroup's LDS.  Measured on
-// MI355X (8B and 70B projections, m = 1..16): the pre-pass wins 4-8 % for long
-// inputs (n_in >= 12288) at 2 <= m <= 8, loses up to 2 us at m = 1 (the extra
-// launch) and loses at m = 16 on long inputs (the copies of many LDS chunks).
+// MI355X over the 8B and 70B projections at m = 1..16 (us, in-kernel ->
+// pre-pass):
+//   - m = 1: the pre-pass loses up to 2 us everywhere (the extra launch);
+//   - n_in = 4096: it loses at m <= 13 (m = 2, 8, 12: 18.5 -> 20.4,
+//     24.3 -> 24.8, 21.0 -> 21.5 on 4096 -> 28672 and 4096 -> 14336) and wins
+//     from m = 14 (22.3 -> 22.1, and 32.0 -> 28.4 at m = 16), where the plan
+//     drops to 4 waves per workgroup and chunks the input;
+//   - n_in = 8192 from m = 4 (16.1 -> 15.9, 20.4 -> 18.9 at m = 8, 32.0 ->
+//     28.2 at m = 16 on 8192 -> 8192) and n_in >= 14336 from m = 2 (equal at
+//     m = 2, 28.1 -> 23.1 at m = 8, 44.6 -> 36.5 at m = 16 on 14336 -> 4096;
+//     57.9 -> 51.8 at m = 4 on 28672 -> 8192): m * n_in >= 28672.
 bool gemv_prerotate(int m, int n_in) {
     static const int force = env_int("EXL3_GEMV_PREROT", -1);
     if (force >= 0) return force > 0;
-    return m >= 2 && m <= 8 && n_in >= GEMV_PREROT_MIN_N_IN;
+    return m >= 2 && (m >= 14 || (n_in >= 8192 && (int64_t)m * n_in >= 28672));
 }
 
 // The bits argument: K in the low byte, the codebook flag above it.

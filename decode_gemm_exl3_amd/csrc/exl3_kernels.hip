@@ -230,9 +230,10 @@ __global__ __launch_bounds__(256) void rotate_gm_kernel(const uint16_t* __restri
 // boundaries, so memory latency is paid once per launch rather than once per
 // strip.  Per-wave partial sums live in LDS (each wave owns its slots, no
 // barrier); at the end the waves' sums are added and y is written.  One kernel,
-// no cross-workgroup reduction.
+// no cross-workgroup reduction.  With PRE the input comes rotated from the
+// pre-pass and is copied into LDS instead of rotated there.
 // ---------------------------------------------------------------------------
-template <int K, int PF, int CB>
+template <int K, int PF, int CB, bool PRE>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     // LDS: x' rows [m][xcols] | zero block [PF * 64] | partial sums [nj][W][m][16]
     extern __shared__ __align__(16) uint32_t xs[];
@@ -329,12 +330,67 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
     // only the x and sign loads and the rotation runs under the weight burst;
     // the scale's latency hides behind the whole stream.
     const int nblk0 = (min(p.kc, p.tiles_in) * 16) >> 7;  // 128-input blocks of chunk 0
-    const bool xpre = !p.xr && (tid >> 4) < M * nblk0;
+    const bool xpre = !PRE && !p.xr && (tid >> 4) < M * nblk0;
     u32x4_t xv0{}, sv0{};
     if (xpre) {
         const int blk = tid >> 4, col = block_col(blk, nblk0, 0);
         xv0 = *reinterpret_cast<const u32x4_t*>(p.x + (int64_t)(blk / nblk0) * p.n_in + col);
         sv0 = *reinterpret_cast<const u32x4_t*>(p.sign + col);
+    }
+    // Pre-rotated input (PRE): a chunk's rows are copied in 16-byte groups of
+    // 8 inputs, taken row by row, XB per thread at a time with their loads
+    // issued together; (xr_row, xr_grp) is the thread's next group.  The first
+    // batch of chunk 0 is loaded here, ahead of the weight burst, so that its
+    // wait does not cover the weight loads.
+    constexpr int XB = 4;
+    struct XBatch {
+        u32x4_t v[XB];
+        int r[XB], c8[XB];
+    };
+    auto xr_first = [&](int per_row, int& r, int& c8) {
+        r = 0;
+        c8 = tid;
+        while (c8 >= per_row && r < M) {
+            c8 -= per_row;
+            ++r;
+        }
+    };
+    auto xr_issue = [&](int tc0, int per_row, int& r, int& c8, XBatch& bt) {
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            bt.r[u] = r;
+            bt.c8[u] = c8;
+            if (r < M) bt.v[u] = *reinterpret_cast<const u32x4_t*>(p.xr + (int64_t)r * p.n_in + tc0 * 16 + c8 * 8);
+            c8 += 64 * W;
+            while (c8 >= per_row && r < M) {
+                c8 -= per_row;
+                ++r;
+            }
+        }
+    };
+    auto xr_store = [&](const XBatch& bt) {
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            if (bt.r[u] < M) {
+                uint32_t d[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w2 = bt.v[u][e];
+                    d[2 * e] = (w2 & 0xFFFFu) | (w2 << 16);  // duplicated for the two codebook halves
+                    d[2 * e + 1] = (w2 >> 16) | (w2 & 0xFFFF0000u);
+                }
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + bt.r[u] * xcols + bt.c8[u] * 8);
+                dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
+                dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+            }
+        }
+    };
+    int xr_row = 0, xr_grp = 0;
+    XBatch xb0;
+    if constexpr (PRE) {
+        const int per_row0 = min(p.kc, p.tiles_in) * 2;
+        xr_first(per_row0, xr_row, xr_grp);
+        xr_issue(0, per_row0, xr_row, xr_grp, xb0);
     }
     uint32_t buf[PF][RowGeom<K>::NB];
     {
@@ -365,24 +421,39 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvParams p) {
         if (c > 0) __syncthreads();  // every wave is done with the previous chunk
         for (int i = kcount * 16 + tid; i < xcols; i += 64 * W)
             for (int r = 0; r < M; ++r) xs[r * xcols + i] = 0u;
-        if (p.xr) {
+        if (PRE || p.xr) {
             // rotated once by the pre-pass: copy the chunk, 8 inputs per lane,
             // each duplicated for the two codebook halves
             const int per_row = kcount * 2;  // 16-byte groups of a row in this chunk
-            for (int r = 0; r < M; ++r)
-                for (int c8 = tid; c8 < per_row; c8 += 64 * W) {
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p.xr + (int64_t)r * p.n_in + tc0 * 16 + c8 * 8);
-                    uint32_t d[8];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t w2 = v[e];
-                        d[2 * e] = (w2 & 0xFFFFu) | (w2 << 16);
-                        d[2 * e + 1] = (w2 >> 16) | (w2 & 0xFFFF0000u);
-                    }
-                    u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + c8 * 8);
-                    dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
-                    dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+            if constexpr (PRE) {
+                if (c == 0)
+                    xr_store(xb0);
+                else
+                    xr_first(per_row, xr_row, xr_grp);
+                while (xr_row < M) {
+                    XBatch bt;
+                    xr_issue(tc0, per_row, xr_row, xr_grp, bt);
+                    xr_store(bt);
                 }
+            } else {
+                // one group per thread at a time: the launcher sends a
+                // pre-rotated input to the PRE instance, so this is reached
+                // only by a direct launch of this one with p.xr set
+                for (int r = 0; r < M; ++r)
+                    for (int c8 = tid; c8 < per_row; c8 += 64 * W) {
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p.xr + (int64_t)r * p.n_in + tc0 * 16 + c8 * 8);
+                        uint32_t d[8];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t w2 = v[e];
+                            d[2 * e] = (w2 & 0xFFFFu) | (w2 << 16);
+                            d[2 * e + 1] = (w2 >> 16) | (w2 & 0xFFFF0000u);
+                        }
+                        u32x4_t* dst = reinterpret_cast<u32x4_t*>(xs + r * xcols + c8 * 8);
+                        dst[0] = u32x4_t{d[0], d[1], d[2], d[3]};
+                        dst[1] = u32x4_t{d[4], d[5], d[6], d[7]};
+                    }
+            }
         } else {
             // chunk 0's first block of each thread was rotated at the start
             const int nblk = (kcount * 16) >> 7;
@@ -512,8 +583,11 @@ hipError_t launch_rotate(const uint16_t* x, const uint16_t* sign, int m, int n_i
     return hipGetLastError();
 }
 
-template <int K, int PF, int CB>
-static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
+// PRE: the input was rotated by the pre-pass (p.xr).  A kernel instance of its
+// own: it carries the batched copy and no rotation code, and the instance that
+// rotates in the kernel keeps the instruction stream it has without them.
+template <int K, int PF, int CB, bool PRE>
+static hipError_t launch_gemv_kpp(const GemvParams& p, hipStream_t s) {
     const size_t lds = gemv_lds_bytes(p.m, p.waves, p.nsw, PF, (p.n_strips + p.grid - 1) / p.grid);
     // allow more than 64 KB of dynamic LDS, once per device
     static std::atomic<unsigned long long> attr_set{0};
@@ -521,13 +595,18 @@ static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     const unsigned long long bit = 1ull << (dev & 63);
     if (!(attr_set.load(std::memory_order_acquire) & bit)) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF, CB>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemv_kernel<K, PF, CB, PRE>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, GEMV_LDS_BUDGET);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((gemv_kernel<K, PF, CB>), dim3(p.grid), dim3(64 * p.waves), lds, s, p);
+    hipLaunchKernelGGL((gemv_kernel<K, PF, CB, PRE>), dim3(p.grid), dim3(64 * p.waves), lds, s, p);
     return hipGetLastError();
+}
+
+template <int K, int PF, int CB>
+static hipError_t launch_gemv_kp(const GemvParams& p, hipStream_t s) {
+    return p.xr ? launch_gemv_kpp<K, PF, CB, true>(p, s) : launch_gemv_kpp<K, PF, CB, false>(p, s);
 }
 
 template <int K, int CB>

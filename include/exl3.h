@@ -116,8 +116,9 @@ int exl3_decode_tile(const uint16_t* words, int32_t bits, int64_t n_tiles,
  *   workspace : optional device scratch (NULL and 0 are accepted).  With at
  *               least m*n_in*2 bytes (rounded up to 256; the size
  *               exl3_pack_info gives for max_m >= m always suffices) an input
- *               of 2..8 rows and n_in >= 12288 is rotated once by a pre-pass
- *               into it; otherwise every workgroup rotates the input itself.
+ *               of m >= 2 rows with m >= 14, or with n_in >= 8192 and
+ *               m * n_in >= 28672, is rotated once by a pre-pass into it;
+ *               otherwise every workgroup rotates the input itself.
  *               Both give the same y bit for bit.  Its contents need no
  *               initialisation and are meaningless after the call; it must not
  *               overlap x, y or the weights.  Calls that may run at the same

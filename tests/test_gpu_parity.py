@@ -214,12 +214,15 @@ def test_gemv_split_and_ragged(torch_cuda):
 
 
 def test_gemv_rotation_pre_pass_and_in_kernel(torch_cuda):
-    # with a workspace a long input of 2..8 rows is rotated once by a pre-pass;
-    # without one every workgroup rotates it: both against the oracle, on
-    # chunked and unchunked inputs, and the two results against each other
+    # with a workspace, an input of m >= 14 rows, or a long one of m >= 2 rows,
+    # is rotated once by a pre-pass; without one every workgroup rotates it:
+    # both against the oracle, on chunked and unchunked inputs, with row counts
+    # that leave the copy's last batch of groups part-filled, and the two
+    # results against each other
     import decode_gemm_exl3_amd as ex
     torch = torch_cuda
-    for (n_in, n_out, K, m) in [(14336, 272, 3, 8), (28672, 64, 2, 2), (12288, 4112, 5, 5), (4096, 528, 4, 16)]:
+    for (n_in, n_out, K, m) in [(14336, 272, 3, 8), (28672, 64, 2, 2), (12288, 4112, 5, 5), (4096, 528, 4, 16),
+                                (8192, 1040, 4, 4), (14336, 4096, 2, 7), (28672, 208, 3, 3), (4096, 1024, 2, 14)]:
         log(f"gemv rotation paths n_in={n_in} n_out={n_out} K={K} m={m}")
         words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [21, n_in, n_out, K, m])
         ref = O.linear(x, words, sign, scale, K)
