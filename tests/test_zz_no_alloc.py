@@ -41,7 +41,7 @@ def rel_fro(y, ref):
 # (n_in, n_out, K, m) pairs: the first call larger than the second.  GEMM with
 # the 256-row kernel and a split input dimension, then the 64-row kernel;
 # the split 128-row kernel, then the GEMV; the GEMV with its rotation pre-pass
-# into the scratch (m = 2..8, n_in >= 12288), then a plain GEMV.
+# into the scratch (m = 8 rows of 14336 inputs), then a plain GEMV.
 SEQUENCES = [
     [(4096, 1024, 3, 300), (4096, 1024, 3, 40)],
     [(2048, 4112, 4, 100), (2048, 4112, 4, 2)],
