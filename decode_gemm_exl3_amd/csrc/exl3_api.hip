@@ -60,15 +60,17 @@ void* noalloc_scratch() {
 }
 
 // Most rows exl3_linear hands to the GEMV.
-constexpr int GEMV_LINEAR_MAX_M = 12;
+constexpr int GEMV_LINEAR_MAX_M = 14;
 
 // Largest rotated GEMM input: it is read through one buffer resource (at most
 // 2^31 - 16 bytes) with 32-bit offsets.
 constexpr int64_t GEMM_MAX_ROT_BYTES = ((int64_t)1 << 31) - ((int64_t)1 << 20);
 
-// exl3_linear's choice of path: the GEMV while m <= 12 and m * n_in <= 2^17.
+// exl3_linear's choice of path: the GEMV while m <= 12 and m * n_in <= 2^17,
+// or m <= 14 and m * n_in <= 2^16.
 bool linear_uses_gemv(int32_t m, int32_t n_in) {
-    return m <= GEMV_LINEAR_MAX_M && (int64_t)m * n_in <= ((int64_t)1 << 17);
+    const int64_t mn = (int64_t)m * n_in;
+    return (m <= 12 && mn <= ((int64_t)1 << 17)) || (m <= GEMV_LINEAR_MAX_M && mn <= ((int64_t)1 << 16));
 }
 
 
@@ -396,11 +398,13 @@ int exl3_gemm(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint1
 int exl3_linear(const uint16_t* x, int32_t m, const uint16_t* trellis, const uint16_t* sign,
                 const uint16_t* out_scale, int32_t n_in, int32_t n_out, int32_t bits, uint16_t* y,
                 void* workspace, size_t workspace_bytes, void* stream) {
-    // Measured crossover (MI355X, K = 4; 4096->14336 and 14336->4096 for
-    // m = 1..16, against the GEMM with 64-row blocks and its split plan): the
-    // GEMV wins through m = 12 at n_in = 4096 and through m = 8 at n_in = 14336
-    // (its x' of the m rows, 4 bytes per input, has to fit the LDS chunks), so
-    // m <= 12 with m * n_in <= 2^17.
+    // Measured crossover (MI355X, K = 4; 4096->14336, 14336->4096 and
+    // 8192->8192 for m = 1..16, against the GEMM with 64-row blocks and its
+    // split plan, the GEMV with its rotation pre-pass where that applies): the
+    // GEMV wins through m = 14 at n_in = 4096 (22.1 against 25.2 us at m = 14,
+    // 28.4 against 25.4 at m = 16), through m = 8 at n_in = 8192 (18.9 against
+    // 24.6; within 2 % at m = 12) and through m = 9 at n_in = 14336 (even at
+    // m = 10), as its x' of the m rows, 4 bytes per input, fills the LDS chunks.
     const bool use_gemv = linear_uses_gemv(m, n_in);
     return use_gemv ? exl3_gemv(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream)
                     : exl3_gemm(x, m, trellis, sign, out_scale, n_in, n_out, bits, y, workspace, workspace_bytes, stream);

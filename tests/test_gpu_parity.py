@@ -460,7 +460,8 @@ def test_gemv_seeded_random_shapes(torch_cuda):
 
 def test_linear_dispatch(torch_cuda):
     # the measured table: GEMV for small m * n_in, the split GEMM beyond
-    for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12)]:
+    for n_in, n_out, K, m in [(1024, 272, 3, 1), (1024, 272, 3, 16), (4096, 48, 4, 33), (14336, 64, 2, 12),
+                              (4096, 528, 4, 14), (2048, 64, 2, 13), (8192, 272, 3, 13)]:
         log(f"linear n_in={n_in} n_out={n_out} K={K} m={m}")
         words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [19, n_in, m])
         y = run_linear(torch_cuda, "linear", words, x, sign, scale, K)
