@@ -222,7 +222,8 @@ def test_gemv_rotation_pre_pass_and_in_kernel(torch_cuda):
     import decode_gemm_exl3_amd as ex
     torch = torch_cuda
     for (n_in, n_out, K, m) in [(14336, 272, 3, 8), (28672, 64, 2, 2), (12288, 4112, 5, 5), (4096, 528, 4, 16),
-                                (8192, 1040, 4, 4), (14336, 4096, 2, 7), (28672, 208, 3, 3), (4096, 1024, 2, 14)]:
+                                (8192, 1040, 4, 4), (14336, 4096, 2, 7), (28672, 208, 3, 3), (4096, 1024, 2, 14),
+                                (28672, 96, 5, 16)]:
         log(f"gemv rotation paths n_in={n_in} n_out={n_out} K={K} m={m}")
         words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [21, n_in, n_out, K, m])
         ref = O.linear(x, words, sign, scale, K)
