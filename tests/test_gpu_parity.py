@@ -146,13 +146,17 @@ def test_decode_codebook1_all_states_k8(torch_cuda):
 @pytest.mark.parametrize("fn", ["gemv", "gemm"])
 def test_linear_codebook1_small_shapes(torch_cuda, fn, K):
     for (n_in, n_out) in [(128, 16), (384, 272), (1024, 1040)]:
-        for m in ((1, 3, 8) if fn == "gemv" else (1, 33, 300)):
+        for m in ((1, 3, 8, 16) if fn == "gemv" else (1, 33, 300)):
             log(f"{fn} codebook 1 K={K} n_in={n_in} n_out={n_out} m={m}")
             words, x, sign, scale = synth.random_case(n_in, n_out, K, m, [17, K, n_in, n_out, m])
             ref = O.linear(x, words, sign, scale, K, cb=1)
             y = run_linear(torch_cuda, fn, words, x, sign, scale, K, cb=1)
             assert np.isfinite(y).all()
             assert_close(y, ref, (fn, K, n_in, n_out, m))
+            if fn == "gemv" and m == 16:  # the pre-rotated instance: same bits
+                import decode_gemm_exl3_amd as ex
+                y_pre = run_linear(torch_cuda, fn, words, x, sign, scale, K, ws=ex.Workspace(n_in, n_out, K, m), cb=1)
+                assert np.array_equal(y_pre.view(np.uint16), y.view(np.uint16)), ("pre-pass", K, n_in, n_out, m)
             if n_in == 1024:  # the codebook is in use: codebook 0 gives another result
                 assert rel_fro(y, O.linear(x, words, sign, scale, K)) > 0.5
 
@@ -197,6 +201,12 @@ def test_linear_small_shapes(torch_cuda, fn, K):
             y = run_linear(torch_cuda, fn, words, x, sign, scale, K)
             assert np.isfinite(y).all()
             assert_close(y, ref, (fn, K, n_in, n_out, m))
+            if fn == "gemv" and m >= 14:
+                # with a workspace these rows are rotated by the pre-pass and
+                # copied (the kernel instance for pre-rotated input): same bits
+                import decode_gemm_exl3_amd as ex
+                y_pre = run_linear(torch_cuda, fn, words, x, sign, scale, K, ws=ex.Workspace(n_in, n_out, K, m))
+                assert np.array_equal(y_pre.view(np.uint16), y.view(np.uint16)), ("pre-pass", K, n_in, n_out, m)
 
 
 def test_gemv_split_and_ragged(torch_cuda):
