@@ -833,6 +833,14 @@ def main():
         extra["single_4096x4096_k4_m1"] = single_layer_rate(torch, ex)
         for m in (1, 4, 8):
             extra[f"mlp_m{m}"] = mlp_rates(torch, ex, m, max(20, args.steps // 4))
+        # the vector-ALU roofline of each m = 1 launch (K = 2, 3, 4): its committed
+        # issue counters over the duration measured here
+        for name, r in extra["mlp_m1"]["launches"].items():
+            p1 = profile_record(f"gemv_mlp8b_m1_{name}.json")
+            if p1 and p1.get("issue"):
+                n = p1["issue"]["valu_insts_without_mfma"]
+                r["alu_frac"] = round(n * 64 / (r["us"] * 1e-6) / VALU_PEAK_LANE_OPS, 4)
+                r["valu_insts_per_launch"] = int(n)
         extra["llama70b_m1"] = llama70b_rates(torch, ex)
         extra["gemm_m2048_8192x8192_k4"] = gemm_rate(torch, ex, "8192_k4")
         extra["gemm_m2048_8192x8192_k4"]["plain_fp16_matmul_same_shape"] = fp16_matmul_tflops(torch)
