@@ -67,6 +67,21 @@ def test_profile_figures_follow_from_raw_fields(path):
         assert i["mfma_busy_frac_at_est_clock"] == pytest.approx(i["mfma_busy_cycles_per_simd"] / se, abs=1e-4)
 
 
+@pytest.mark.parametrize("path", PROFILES, ids=os.path.basename)
+def test_kernel_stats_agree_with_profile(path):
+    # the rocprofv3 --stats summary committed beside each profile: the same
+    # kernel, dispatch count and average duration as the trace summary
+    rec = json.load(open(path))
+    stats = path[:-len(".json")] + "_kernel_stats.txt"
+    assert os.path.exists(stats), f"{os.path.basename(stats)} missing"
+    lines = [ln for ln in open(stats) if not ln.startswith("#")]
+    rows = {r["Name"]: r for r in csv.DictReader(lines)}
+    row = rows[rec["kernel"]]
+    assert int(row["Calls"]) == rec["dispatches"]
+    assert float(row["AverageNs"]) == pytest.approx(rec["mean_ns"], abs=1.0)
+    assert int(row["MinNs"]) == rec["min_ns"] and int(row["MaxNs"]) == rec["max_ns"]
+
+
 def _write_csv(path, fields, rows):
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=fields)
