@@ -340,10 +340,10 @@ def test_zero_m_is_noop(torch_cuda):
 
 
 # ------------------------------------------- fused multi-projection GEMV -----
-def run_multi(torch, words, x, sign, scales, K):
+def run_multi(torch, words, x, sign, scales, K, ws=None):
     import decode_gemm_exl3_amd as ex
     ys = ex.gemv_multi(to_dev(torch, x), [(to_dev(torch, w), to_dev(torch, sc)) for w, sc in zip(words, scales)],
-                       to_dev(torch, sign), K)
+                       to_dev(torch, sign), K, workspace=ws)
     torch.cuda.synchronize()
     return [y.cpu().numpy() for y in ys]
 
@@ -363,6 +363,16 @@ def test_gemv_multi_small_shapes(torch_cuda, K):
             for i, (w, sc, y) in enumerate(zip(words, scales, ys)):
                 assert y.shape == (m, sc.shape[0])
                 assert_close(y, O.linear(x, w, sign, sc, K), (K, n_in, n_outs, m, i))
+    # 16 rows with a workspace: the pre-pass and the pre-rotated instance over
+    # several projections, bit for bit the in-kernel rotation's result
+    import decode_gemm_exl3_amd as ex
+    n_in, n_outs, m = 1024, (64, 1040, 16, 48), 16
+    words, x, sign, scales = group_case(n_in, n_outs, K, m, 310 + K)
+    ys = run_multi(torch_cuda, words, x, sign, scales, K)
+    ys_pre = run_multi(torch_cuda, words, x, sign, scales, K, ws=ex.Workspace(n_in, max(n_outs), K, m))
+    for i, (w, sc, y, yp) in enumerate(zip(words, scales, ys, ys_pre)):
+        assert_close(y, O.linear(x, w, sign, sc, K), (K, n_in, n_outs, m, i))
+        assert np.array_equal(yp.view(np.uint16), y.view(np.uint16)), ("pre-pass", K, i)
 
 
 def test_gemv_multi_matches_separate_calls(torch_cuda):
