@@ -829,6 +829,8 @@ def main():
                "frac": round(a / VALU_PEAK_LANE_OPS, 4), "valu_insts_per_launch": int(n)}
 
     extra = {"stack_launch_shapes": shapes, "copy_gbs": copy_bandwidth(torch)}
+    # what a plain device copy reaches on this part, beside the spec peak
+    roofline["frac_of_copy_rate"] = round(achieved / extra["copy_gbs"], 4)
     if not args.no_extra:
         extra["single_4096x4096_k4_m1"] = single_layer_rate(torch, ex)
         for m in (1, 4, 8):
