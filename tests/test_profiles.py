@@ -144,3 +144,25 @@ def test_sources_hash_ignores_comments_only(tmp_path, monkeypatch):
     assert bench.kernel_sources_hash(("k.hip",)) == h1
     (csrc / "k.hip").write_text("int f() { return 2; }\nint g();\n")
     assert bench.kernel_sources_hash(("k.hip",)) != h1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_trace_summary_of_synthetic_trace(tmp_path, capsys):
+    path = tmp_path / "k_kernel_trace.csv"
+    _write_csv(path, ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+               [{"Kernel_Name": "a", "Start_Timestamp": 0, "End_Timestamp": 300},
+                {"Kernel_Name": "a", "Start_Timestamp": 400, "End_Timestamp": 500},
+                {"Kernel_Name": "b", "Start_Timestamp": 600, "End_Timestamp": 700}])
+    bench.trace_summary(str(path))
+    lines = capsys.readouterr().out.strip().splitlines()
+    assert lines[0].startswith("# columns")
+    # kernels by total time: a (2 calls, median 200 ns, 80 %), then b
+    assert lines[1] == "a | 2 | 200 | 200 | 100 | 300 | 80.00"
+    assert lines[2] == "b | 1 | 100 | 100 | 100 | 100 | 20.00"
